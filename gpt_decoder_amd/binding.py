@@ -1,0 +1,291 @@
+"""ctypes binding of libngpt (the C ABI in include/ngpt.h).
+
+Argument marshalling only: every step of the forward pass and the sampler
+runs in the library's HIP kernels.  PyTorch provides device memory (weights,
+KV cache, ids, uniforms, outputs) and the stream.  There is no CPU fallback:
+importing this module without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libngpt.so")
+
+NGPT_OK = 0
+NGPT_E_ARG = -1
+NGPT_E_CONFIG = -2
+NGPT_E_RANGE = -3
+NGPT_E_SIZE = -4
+NGPT_E_CONTEXT = -5
+NGPT_E_HIP = -6
+NGPT_E_DEVICE = -7
+NGPT_F32 = 0
+NGPT_BF16 = 1
+NGPT_MAX_BATCH = 256
+
+
+class NgptError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_status_name(code)} ({code}): {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layer", "n_head", "n_embd", "block_size", "vocab_size", "bias",
+        "dtype", "max_batch", "max_prefill_tokens")]
+
+
+_LAYER_FIELDS = ("ln1_w", "ln1_b", "attn_w", "attn_b", "attnproj_w",
+                 "attnproj_b", "ln2_w", "ln2_b", "fc_w", "fc_b", "mlpproj_w",
+                 "mlpproj_b")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _LAYER_FIELDS]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("wte", ctypes.c_void_p), ("wpe", ctypes.c_void_p),
+                ("lnf_w", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights))]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("lens", ctypes.c_void_p), ("limit", ctypes.c_void_p),
+                ("batch", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libngpt.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m "
+            "gpt_decoder_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.ngpt_kv_bytes.argtypes = [ctypes.POINTER(Config), i32]
+    L.ngpt_kv_bytes.restype = sz
+    L.ngpt_check_config.argtypes = [ctypes.POINTER(Config)]
+    L.ngpt_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                              vp, ctypes.POINTER(vp)]
+    L.ngpt_destroy.argtypes = [vp]
+    L.ngpt_set_sampling.argtypes = [vp, ctypes.c_float, i32, i32]
+    L.ngpt_prefill.argtypes = [vp, ctypes.POINTER(KV), vp,
+                               ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
+                               i32]
+    L.ngpt_decode_step.argtypes = [vp, ctypes.POINTER(KV), vp, vp]
+    L.ngpt_decode_feed.argtypes = [vp, ctypes.POINTER(KV), vp]
+    L.ngpt_sample.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.ngpt_logits.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i32)]
+    L.ngpt_copy_logits.argtypes = [vp, vp, i32, i32]
+    L.ngpt_device_status.argtypes = [vp, ctypes.POINTER(i32)]
+    L.ngpt_last_error.argtypes = [vp]
+    L.ngpt_last_error.restype = ctypes.c_char_p
+    L.ngpt_status_string.argtypes = [ctypes.c_int]
+    L.ngpt_status_string.restype = ctypes.c_char_p
+    for name in ("ngpt_check_config", "ngpt_create", "ngpt_destroy",
+                 "ngpt_set_sampling", "ngpt_prefill", "ngpt_decode_step",
+                 "ngpt_decode_feed", "ngpt_sample", "ngpt_logits",
+                 "ngpt_copy_logits", "ngpt_device_status"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _status_name(code: int) -> str:
+    try:
+        return lib().ngpt_status_string(code).decode()
+    except Exception:
+        return str(code)
+
+
+def make_config(n_layer, n_head, n_embd, block_size, vocab_size, bias, dtype,
+                max_batch, max_prefill_tokens) -> Config:
+    d = {"f32": NGPT_F32, "bf16": NGPT_BF16}.get(dtype, dtype)
+    return Config(n_layer, n_head, n_embd, block_size, vocab_size, int(bias),
+                  d, max_batch, max_prefill_tokens)
+
+
+def kv_bytes(cfg: Config, batch: int) -> int:
+    return int(lib().ngpt_kv_bytes(ctypes.byref(cfg), batch))
+
+
+def check_config(cfg: Config) -> int:
+    return int(lib().ngpt_check_config(ctypes.byref(cfg)))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+class KVCache:
+    """Caller-owned KV cache: K and V [L][B][H][Tb][hs] plus lens/limit."""
+
+    def __init__(self, cfg: Config, batch: int, device="cuda"):
+        import torch
+        nbytes = kv_bytes(cfg, batch)
+        if nbytes == 0 and cfg.n_layer > 0:
+            raise NgptError(NGPT_E_CONFIG, "invalid config for the KV cache")
+        n = max(nbytes, 16)
+        self.k = torch.empty(n, dtype=torch.uint8, device=device)
+        self.v = torch.empty(n, dtype=torch.uint8, device=device)
+        self.lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.limit = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.batch = batch
+        self.struct = KV(_ptr(self.k), _ptr(self.v), _ptr(self.lens),
+                         _ptr(self.limit), batch)
+
+
+class Model:
+    """A libngpt model handle bound to one stream.
+
+    ``weights`` is a dict in nn.Linear layout (see ``synth.make_weights``):
+    numpy or torch arrays; they are uploaded once to the device in the model
+    dtype and kept alive here for the handle's lifetime.
+    """
+
+    def __init__(self, *, n_layer, n_head, n_embd, block_size, vocab_size,
+                 bias, dtype, weights, max_batch, max_prefill_tokens,
+                 device="cuda", stream=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device)
+        self.cfg = make_config(n_layer, n_head, n_embd, block_size, vocab_size,
+                               bias, dtype, max_batch, max_prefill_tokens)
+        self.vocab = vocab_size
+        tdt = torch.bfloat16 if self.cfg.dtype == NGPT_BF16 else torch.float32
+        keep = []
+
+        def up(a):
+            if a is None:
+                return None
+            t = torch.as_tensor(np.asarray(a) if not torch.is_tensor(a) else a)
+            t = t.to(device=self.device, dtype=tdt).contiguous()
+            keep.append(t)
+            return t
+
+        layers = (LayerWeights * max(1, n_layer))()
+        for l, lw in enumerate(weights["layers"]):
+            for f in _LAYER_FIELDS:
+                setattr(layers[l], f, _ptr(up(lw[f])))
+        self._weights = Weights(_ptr(up(weights["wte"])),
+                                _ptr(up(weights["wpe"])),
+                                _ptr(up(weights["lnf_w"])),
+                                _ptr(up(weights["lnf_b"])), layers)
+        self._layers = layers
+        self._keep = keep
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self.stream = stream
+        h = ctypes.c_void_p()
+        rc = lib().ngpt_create(ctypes.byref(self.cfg),
+                               ctypes.byref(self._weights),
+                               ctypes.c_void_p(stream.cuda_stream),
+                               ctypes.byref(h))
+        if rc != NGPT_OK:
+            raise NgptError(rc, lib().ngpt_last_error(None).decode())
+        self.h = h
+
+    # -- helpers -----------------------------------------------------------
+    def _check(self, rc):
+        if rc != NGPT_OK:
+            raise NgptError(rc, lib().ngpt_last_error(self.h).decode())
+
+    def new_kv(self, batch: int) -> KVCache:
+        return KVCache(self.cfg, batch, self.device)
+
+    # -- the C calls ---------------------------------------------------------
+    def set_sampling(self, temperature=1.0, top_k=0, greedy=False):
+        self._check(lib().ngpt_set_sampling(self.h, float(temperature),
+                                            int(top_k), int(bool(greedy))))
+
+    def prefill(self, kv: KVCache, ids, lens: Sequence[int],
+                limit: Optional[Sequence[int]] = None):
+        """``ids``: device int32 [B, Tmax]; ``lens``/``limit``: host ints."""
+        B, Tmax = ids.shape
+        assert ids.dtype == self.torch.int32 and ids.is_contiguous()
+        lens_a = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+        lim_a = None if limit is None else (ctypes.c_int32 * B)(
+            *[int(x) for x in limit])
+        self._check(lib().ngpt_prefill(self.h, ctypes.byref(kv.struct),
+                                       _ptr(ids), lens_a, lim_a, B, Tmax))
+
+    def decode_step(self, kv: KVCache, next_ids, uniforms):
+        """``next_ids``: device int32 [batch] (out); ``uniforms``: device
+        float64 [batch]."""
+        assert next_ids.dtype == self.torch.int32
+        assert uniforms is None or uniforms.dtype == self.torch.float64
+        self._check(lib().ngpt_decode_step(self.h, ctypes.byref(kv.struct),
+                                           _ptr(next_ids), _ptr(uniforms)))
+
+    def decode_feed(self, kv: KVCache, ids):
+        assert ids.dtype == self.torch.int32
+        self._check(lib().ngpt_decode_feed(self.h, ctypes.byref(kv.struct),
+                                           _ptr(ids)))
+
+    def sample(self, logits, uniforms=None, out=None):
+        """Sampler alone on device fp32 logits [B, ld]; returns int32 [B]."""
+        B, ld = logits.shape
+        assert logits.dtype == self.torch.float32 and logits.is_contiguous()
+        if out is None:
+            out = self.torch.empty(B, dtype=self.torch.int32,
+                                   device=self.device)
+        self._check(lib().ngpt_sample(self.h, _ptr(logits), ld, B,
+                                      _ptr(uniforms), _ptr(out)))
+        return out
+
+    def logits(self, B: int, out=None):
+        """Copy of the first B logits rows (device fp32 [B, vocab])."""
+        if out is None:
+            out = self.torch.empty((B, self.vocab), dtype=self.torch.float32,
+                                   device=self.device)
+        self._check(lib().ngpt_copy_logits(self.h, _ptr(out), out.shape[1], B))
+        return out
+
+    def logits_ptr(self):
+        p, ld = ctypes.c_void_p(), ctypes.c_int32()
+        self._check(lib().ngpt_logits(self.h, ctypes.byref(p), ctypes.byref(ld)))
+        return p.value, ld.value
+
+    def device_status(self) -> int:
+        st = ctypes.c_int32()
+        self._check(lib().ngpt_device_status(self.h, ctypes.byref(st)))
+        return st.value
+
+    def close(self):
+        if getattr(self, "h", None):
+            rc = lib().ngpt_destroy(self.h)
+            self.h = None
+            if rc != NGPT_OK:
+                raise NgptError(rc, lib().ngpt_last_error(None).decode())
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def model_from_workload(w, weights, *, max_batch=None, max_prefill_tokens=None,
+                        device="cuda", stream=None) -> Model:
+    """Model for a ``synth.Workload``-like shape description."""
+    mb = max_batch or w.batch
+    mpt = max_prefill_tokens or mb * w.block_size
+    return Model(n_layer=len(weights["layers"]), n_head=w.n_head,
+                 n_embd=w.n_embd, block_size=w.block_size,
+                 vocab_size=w.vocab_size, bias=weights["lnf_b"] is not None,
+                 dtype=w.dtype, weights=weights, max_batch=mb,
+                 max_prefill_tokens=mpt, device=device, stream=stream)

@@ -1,0 +1,113 @@
+// Host-side launchers of the libngpt kernels and their argument records.
+// Every launcher enqueues on the given stream and returns immediately.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ngpt.h"
+
+namespace ngpt {
+
+// Packed prefill rows: sequence b owns rows [off[b], off[b+1]).
+struct RowMap {
+  int32_t B;
+  int32_t off[NGPT_MAX_BATCH + 1];
+};
+
+// Linear-layer epilogues (what happens to acc = A W^T for row r, column n).
+enum Epi {
+  EPI_STORE = 0,   // out[r][n] = acc + bias                      (dtype)
+  EPI_GELU = 1,    // out[r][n] = GELU(acc + bias)                (dtype)
+  EPI_RESID = 2,   // out[r][n] += acc + bias                      (fp32 residual)
+  EPI_QKV = 3,     // split into q (out, dtype) and the K/V cache rows
+  EPI_LOGITS = 4,  // out[r][n] = acc                             (fp32)
+};
+
+struct EpiArgs {
+  const void* bias = nullptr;     // [N] dtype or null
+  void* out = nullptr;
+  int ldo = 0;
+  // EPI_QKV: this layer's cache, each [batch][H][Tb][hs]
+  void* kc = nullptr;
+  void* vc = nullptr;
+  const int32_t* row_b = nullptr;    // row -> sequence (null: identity)
+  const int32_t* row_pos = nullptr;  // row -> position; < 0 => inactive row
+  int C = 0, H = 0, hs = 0, Tb = 0;
+};
+
+// Sampling parameters, resident in device memory so that a captured decode
+// graph picks up changes.
+struct SampleParams {
+  float temperature;
+  int32_t top_k;
+  int32_t greedy;
+  int32_t pad;
+};
+
+enum SampleMode {
+  SAMPLE_ONLY = 0,  // write next_ids only
+  SAMPLE_STEP = 1,  // decode step: also tok/pos, advance lens
+  FEED_STEP = 2,    // teacher forcing: ids given, set tok/pos, advance lens
+};
+
+void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
+                          const RowMap& map, int M, const void* wte,
+                          const void* wpe, int C, int V, float* x,
+                          int32_t* row_b, int32_t* row_pos, int32_t* last_rows,
+                          int32_t* status, hipStream_t s);
+
+void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,
+                         int B, const void* wte, const void* wpe, int C, int V,
+                         float* x, int32_t* status, hipStream_t s);
+
+// out[i] = LN(x[rows ? rows[i] : i]) over C columns, fp32 statistics.
+void launch_layernorm(int dtype, const float* x, int ldx, const int32_t* rows,
+                      int M, const void* w, const void* b, void* out, int ldo,
+                      int C, hipStream_t s);
+
+// acc = A[M][K] W[N][K]^T, then the epilogue.  A and W are dtype.
+void launch_linear(int dtype, int epi, const void* A, int lda, const void* W,
+                   int M, int N, int K, const EpiArgs& e, hipStream_t s);
+
+// Causal attention of each packed prefill row against its own sequence's
+// keys in the cache (positions 0..pos).  q is [M][ldq] (head j at columns
+// j*hs), the output y [M][ldy] likewise.
+void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
+                         const void* vc, const RowMap& map, int maxlen, int H,
+                         int hs, int Tb, void* y, int ldy, hipStream_t s);
+
+// One query per active sequence (pos[b] >= 0) against cache rows
+// 0..pos[b], split over key chunks with a cross-workgroup combine.
+int attn_decode_chunks(int Tb);
+void launch_attn_decode(int dtype, const void* q, const void* kc,
+                        const void* vc, const int32_t* pos, int B, int H,
+                        int hs, int Tb, float* part, int32_t* counters,
+                        void* y, hipStream_t s);
+
+// Argument pack of the sampler kernel, used to (re)write its graph node.
+struct SamplerArgs {
+  int mode = 0;
+  const float* logits = nullptr;
+  int ld = 0;
+  int V = 0;
+  const double* uniforms = nullptr;
+  const SampleParams* params = nullptr;
+  const int32_t* feed_ids = nullptr;
+  int32_t* next_ids = nullptr;
+  int32_t* tok = nullptr;
+  int32_t* pos = nullptr;
+  int32_t* lens = nullptr;
+  const int32_t* limit = nullptr;
+  int32_t* status = nullptr;
+  void* ptrs[13] = {};
+};
+// Fill a kernel-node description for B rows; `a` must outlive its use.
+void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
+
+void launch_sampler(int mode, const float* logits, int ld, int B, int V,
+                    const double* uniforms, const SampleParams* params,
+                    const int32_t* feed_ids, int32_t* next_ids, int32_t* tok,
+                    int32_t* pos, int32_t* lens, const int32_t* limit,
+                    int32_t* status, hipStream_t s);
+
+}  // namespace ngpt

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: logits max-abs 1e-4 (fp32 model) or 2e-2 (bf16 model); sampled ids
+and top-k sets bit-exact on identical logits and uniforms (draws whose
+running-sum margin is below 1e-12 of the total are reported, not failed);
+greedy ids identical on every teacher-forced step whose oracle top-1/top-2
+gap exceeds twice the logit tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import (TOL_BF16, TOL_F32, Timer, dev_f64, dev_i32, gpu_prefill,
+                        log, make_model, make_oracle, max_abs, need_gpu, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# tiny character model, fp32: free-running greedy generation end to end
+# ---------------------------------------------------------------------------
+
+def test_char_4l128_fp32_greedy_generation():
+    torch = need_gpu()
+    w = synth.workload("char_4l128_fp32")
+    W = synth.make_weights(w)
+    ids, lens = synth.make_prompts(w)
+    log("char_4l128_fp32: prefill 16 + 48 greedy steps")
+    o = make_oracle(w, W)
+    ref_toks, ref_logits = o.generate_greedy(list(ids[0, :lens[0]]), w.steps)
+
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(1)
+    lg = gpu_prefill(m, kv, ids, lens)
+    assert max_abs(lg[0], ref_logits[0]) < TOL_F32
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    toks, errs = [], []
+    for s in range(w.steps):
+        if s > 0:
+            errs.append(max_abs(m.logits(1).cpu().numpy()[0], ref_logits[s]))
+        m.decode_step(kv, nxt, None)
+        toks.append(int(nxt.item()))
+        if toks[-1] != ref_toks[s]:
+            break
+    log(f"  max logit err {max(errs):.2e}")
+    assert toks == ref_toks
+    assert max(errs) < TOL_F32
+    assert kv.lens.cpu().tolist() == [16 + 48]
+    assert m.device_status() == 0
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# Shakespeare-char shape, bf16, batch 8: prefill + teacher-forced decode
+# ---------------------------------------------------------------------------
+
+def test_char_6l384_bf16_prefill_and_feed():
+    torch = need_gpu()
+    w = synth.workload("char_6l384_bf16_b8")
+    W = synth.make_weights(w)
+    ids, lens = synth.make_prompts(w)
+    steps = 24
+    feed = synth.make_feed_tokens(w, steps)
+    log("char_6l384_bf16_b8: prefill 8x64 + 24 fed steps")
+    o = make_oracle(w, W)
+    ref = [o.prefill(ids, lens)]
+    for s in range(steps):
+        ref.append(o.decode(feed[s]))
+    m = make_model(w, W)
+    kv = m.new_kv(w.batch)
+    got = [gpu_prefill(m, kv, ids, lens)]
+    for s in range(steps):
+        m.decode_feed(kv, dev_i32(feed[s]))
+        got.append(m.logits(w.batch).cpu().numpy())
+    errs = [max_abs(a, b) for a, b in zip(got, ref)]
+    log(f"  max logit err per step: first {errs[0]:.2e} max {max(errs):.2e}")
+    assert max(errs) < TOL_BF16
+    assert kv.lens.cpu().tolist() == [64 + steps] * 8
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# GPT-2 124M shape, bf16: prefill 128 and a few fed decode steps
+# ---------------------------------------------------------------------------
+
+def test_gpt2_124m_prefill_and_feed_short():
+    need_gpu()
+    w = synth.workload("gpt2_124m_b1")
+    W = synth.make_weights(w)
+    ids, lens = synth.make_prompts(w)
+    feed = synth.make_feed_tokens(w, 8)
+    log("gpt2_124m_b1: prefill 128 + 8 fed steps")
+    o = make_oracle(w, W)
+    ref = [o.prefill(ids, lens)] + [o.decode(feed[s]) for s in range(8)]
+    m = make_model(w, W)
+    kv = m.new_kv(1)
+    got = [gpu_prefill(m, kv, ids, lens)]
+    for s in range(8):
+        m.decode_feed(kv, dev_i32(feed[s]))
+        got.append(m.logits(1).cpu().numpy())
+    errs = [max_abs(a, b) for a, b in zip(got, ref)]
+    log(f"  logit errs {['%.1e' % e for e in errs]}")
+    assert max(errs) < TOL_BF16
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# sampler on identical logits
+# ---------------------------------------------------------------------------
+
+SAMPLER_CASES = [
+    # (B, V, temperature, top_k, greedy, ties)
+    (8, 65, 0.8, 200, False, 0),
+    (8, 65, 0.8, 200, False, 6),
+    (64, 50304, 1.0, 50, False, 0),
+    (64, 50304, 1.0, 50, False, 40),
+    (16, 50304, 0.7, 0, False, 0),
+    (16, 50304, 1.3, 1, False, 5),
+    (32, 50304, 1.0, 0, True, 0),
+    (32, 50304, 1.0, 0, True, 8),
+    (4, 1, 1.0, 5, False, 0),
+]
+
+
+@pytest.mark.parametrize("B,V,T,k,greedy,ties", SAMPLER_CASES)
+def test_sampler_bit_exact(B, V, T, k, greedy, ties):
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    w = synth.Workload("sampler", 7, 0, 1, 64, 8, V, V, False, "bf16",
+                       batch=B, prompt_len=1)
+    W = synth.make_weights(w)
+    m = make_model(w, W, max_batch=B)
+    m.set_sampling(temperature=T, top_k=k, greedy=greedy)
+    lg = synth.make_logits(B, V, seed=V * 7 + B + ties, ties=ties)
+    uni = np.random.default_rng(B + V).random(B)
+    uni[0] = 0.0
+    ids = m.sample(torch.from_numpy(lg).cuda(), dev_f64(uni)).cpu().numpy()
+    ref, _, margins = oracle.sample_rows(lg, uni, T, k, greedy)
+    flagged = (margins < 1e-12) if not greedy else np.zeros(B, bool)
+    log(f"  B={B} V={V} T={T} k={k} greedy={greedy}: flagged {flagged.sum()}")
+    np.testing.assert_array_equal(ids[~flagged], ref[~flagged])
+    m.close()
+
+
+@pytest.mark.parametrize("V,k,ties", [(50304, 50, 0), (50304, 50, 30), (65, 200, 4),
+                                      (1000, 7, 12)])
+def test_sampler_topk_set_exact(V, k, ties):
+    """Recover the kept set from the GPU by sweeping u across [0,1) on a
+    high temperature (near-uniform kept mass) and compare it with the
+    oracle's set."""
+    torch = need_gpu()
+    B = 256
+    w = synth.Workload("sampler", 7, 0, 1, 64, 8, V, V, False, "bf16",
+                       batch=B, prompt_len=1)
+    m = make_model(w, synth.make_weights(w), max_batch=B)
+    T = 1000.0
+    m.set_sampling(temperature=T, top_k=k, greedy=False)
+    row = synth.make_logits(1, V, seed=99 + ties, ties=ties)
+    if ties:   # force ties exactly at the k-th value
+        s = np.sort(row[0])[::-1]
+        row[0, np.argsort(row[0])[:3]] = s[min(k, V) - 1]
+    lg = np.repeat(row, B, axis=0)
+    uni = (np.arange(B) + 0.5) / B
+    ids = m.sample(torch.from_numpy(lg).cuda(), dev_f64(uni)).cpu().numpy()
+    _, keep, _ = oracle.sample_row(row[0], 0.5, T, k, False)
+    want = set(np.nonzero(keep)[0].tolist())
+    assert len(want) < B // 3
+    assert set(ids.tolist()) == want
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# 1024-token prefill, GPT-2 124M shape
+# ---------------------------------------------------------------------------
+
+def test_gpt2_124m_prefill_1024():
+    need_gpu()
+    w = synth.workload("gpt2_124m_prefill1024")
+    W = synth.make_weights(w)
+    ids, lens = synth.make_prompts(w)
+    log("gpt2_124m_prefill1024")
+    with Timer("  oracle 1024-token forward"):
+        ref = make_oracle(w, W).prefill(ids, lens)
+    m = make_model(w, W)
+    kv = m.new_kv(1)
+    got = gpu_prefill(m, kv, ids, lens)
+    e = max_abs(got, ref)
+    log(f"  logit err {e:.2e}")
+    assert e < TOL_BF16
+    m.close()
