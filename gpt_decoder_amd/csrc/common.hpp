@@ -63,4 +63,18 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
 }
 
+// Merge two partial softmax states (running max m in the log2 domain, sum l,
+// weighted value sums o[n]) into the first.
+__device__ __forceinline__ void merge_state(float& m, float& l, float* o,
+                                            float m2, float l2,
+                                            const float* o2, int n) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+  const float c = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
+  l = l * a + l2 * c;
+  for (int j = 0; j < n; ++j) o[j] = o[j] * a + o2[j] * c;
+  m = mn;
+}
+
 }  // namespace ngpt

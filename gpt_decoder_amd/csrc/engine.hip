@@ -94,7 +94,6 @@ struct ngpt_model {
   float* logits = nullptr;
   int32_t *row_b = nullptr, *row_pos = nullptr, *last_rows = nullptr;
   float* part = nullptr;
-  int32_t* counters = nullptr;
   int32_t *tok = nullptr, *pos = nullptr, *status = nullptr;
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
@@ -128,6 +127,7 @@ static int check_config(const ngpt_config* c, std::string* why) {
   if (c->dtype != NGPT_F32 && c->dtype != NGPT_BF16) return bad("unknown dtype");
   if (c->dtype == NGPT_BF16 && c->n_embd % 64 != 0) return bad("bf16 needs n_embd % 64 == 0");
   if (c->dtype == NGPT_F32 && c->n_embd % 4 != 0) return bad("fp32 needs n_embd % 4 == 0");
+  if (c->n_embd > 2048) return bad("n_embd must be <= 2048");
   if (c->block_size < 1 || c->block_size > 4096) return bad("block_size must be in [1, 4096]");
   if (c->vocab_size < 1) return bad("vocab_size must be >= 1");
   if (c->bias != 0 && c->bias != 1) return bad("bias must be 0 or 1");
@@ -207,7 +207,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
                o_lg = carve(Bm * (size_t)m->V * 4), o_rb = carve(Mm * 4),
                o_rp = carve(Mm * 4), o_lr = carve(Bm * 4),
                o_part = carve(Bm * m->H * (size_t)m->nchunk * (m->hs + 2) * 4),
-               o_cnt = carve(Bm * m->H * 4), o_tok = carve(Bm * 4),
+               o_tok = carve(Bm * 4),
                o_pos = carve(Bm * 4), o_st = carve(16),
                o_prm = carve(sizeof(SampleParams));
   hipError_t e = hipMalloc(&m->ws, off);
@@ -221,7 +221,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
   m->logits = (float*)(base + o_lg);
   m->row_b = (int32_t*)(base + o_rb); m->row_pos = (int32_t*)(base + o_rp);
   m->last_rows = (int32_t*)(base + o_lr); m->part = (float*)(base + o_part);
-  m->counters = (int32_t*)(base + o_cnt); m->tok = (int32_t*)(base + o_tok);
+  m->tok = (int32_t*)(base + o_tok);
   m->pos = (int32_t*)(base + o_pos); m->status = (int32_t*)(base + o_st);
   m->params = (SampleParams*)(base + o_prm);
   e = hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking);
@@ -328,30 +328,30 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, kv->batch);
     void* vl = layer_cache(m, kv->v, l, kv->batch);
-    launch_layernorm(dt, m->x, C, nullptr, M, w.ln1_w, w.ln1_b, m->h, C, C, s);
+    const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = m->row_b; eq.row_pos = m->row_pos;
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
-    launch_linear(dt, EPI_QKV, m->h, C, w.attn_w, M, 3 * C, C, eq, s);
+    launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, M, 3 * C, C, eq, s);
     launch_attn_prefill(dt, m->q, C, kl, vl, map, maxlen, m->H, m->hs, m->Tb,
                         m->y, C, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
-    launch_linear(dt, EPI_RESID, m->y, C, w.attnproj_w, M, C, C, ep, s);
-    launch_layernorm(dt, m->x, C, nullptr, M, w.ln2_w, w.ln2_b, m->h, C, C, s);
+    launch_linear(dt, EPI_RESID, m->y, C, nullptr, w.attnproj_w, M, C, C, ep, s);
+    const LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
     EpiArgs ef;
     ef.bias = w.fc_b; ef.out = m->f; ef.ldo = 4 * C;
-    launch_linear(dt, EPI_GELU, m->h, C, w.fc_w, M, 4 * C, C, ef, s);
+    launch_linear(dt, EPI_GELU, nullptr, C, &ln2, w.fc_w, M, 4 * C, C, ef, s);
     EpiArgs em;
     em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
-    launch_linear(dt, EPI_RESID, m->f, 4 * C, w.mlpproj_w, M, C, 4 * C, em, s);
+    launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, M, C, 4 * C, em, s);
   }
   // ln_f and the tied lm_head on each sequence's last row only
   launch_layernorm(dt, m->x, C, m->last_rows, B, m->lnf_w, m->lnf_b, m->z, C, C, s);
   EpiArgs el;
   el.out = m->logits; el.ldo = m->V;
-  launch_linear(dt, EPI_LOGITS, m->z, C, m->wte, B, m->V, C, el, s);
+  launch_linear(dt, EPI_LOGITS, m->z, C, nullptr, m->wte, B, m->V, C, el, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
 
@@ -361,38 +361,43 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
   return NGPT_OK;
 }
 
-// The one-token forward shared by the step and feed graphs (after the head
-// node has set tok/pos and advanced lens).
+// The one-token forward shared by the step and feed graphs.  The head node
+// (sampler or feed) has already set tok/pos, advanced lens and written the
+// embedding x = wte[tok] + wpe[pos] of every row.
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
-  launch_embed_decode(dt, m->tok, m->pos, Bk, m->wte, m->wpe, C, m->V, m->x, m->status, s);
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, Bk);
     void* vl = layer_cache(m, kv->v, l, Bk);
-    launch_layernorm(dt, m->x, C, nullptr, Bk, w.ln1_w, w.ln1_b, m->h, C, C, s);
+    const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = nullptr; eq.row_pos = m->pos;
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
-    launch_linear(dt, EPI_QKV, m->h, C, w.attn_w, Bk, 3 * C, C, eq, s);
+    launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, Bk, 3 * C, C, eq, s);
+    const bool fused = decode_fused_proj(Bk);
     launch_attn_decode(dt, m->q, kl, vl, m->pos, Bk, m->H, m->hs, m->Tb,
-                       m->part, m->counters, m->y, s);
+                       m->part, m->y, !fused, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
-    launch_linear(dt, EPI_RESID, m->y, C, w.attnproj_w, Bk, C, C, ep, s);
-    launch_layernorm(dt, m->x, C, nullptr, Bk, w.ln2_w, w.ln2_b, m->h, C, C, s);
+    if (fused)
+      launch_attn_proj(dt, m->part, m->pos, m->H, m->hs, m->nchunk,
+                       attn_decode_chunk_keys(), w.attnproj_w, Bk, C, ep, s);
+    else
+      launch_linear(dt, EPI_RESID, m->y, C, nullptr, w.attnproj_w, Bk, C, C, ep, s);
+    const LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
     EpiArgs ef;
     ef.bias = w.fc_b; ef.out = m->f; ef.ldo = 4 * C;
-    launch_linear(dt, EPI_GELU, m->h, C, w.fc_w, Bk, 4 * C, C, ef, s);
+    launch_linear(dt, EPI_GELU, nullptr, C, &ln2, w.fc_w, Bk, 4 * C, C, ef, s);
     EpiArgs em;
     em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
-    launch_linear(dt, EPI_RESID, m->f, 4 * C, w.mlpproj_w, Bk, C, 4 * C, em, s);
+    launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, Bk, C, 4 * C, em, s);
   }
-  launch_layernorm(dt, m->x, C, nullptr, Bk, m->lnf_w, m->lnf_b, m->z, C, C, s);
+  const LnArgs lnf{m->x, C, m->lnf_w, m->lnf_b, m->z};
   EpiArgs el;
   el.out = m->logits; el.ldo = m->V; el.row_pos = m->pos;
-  launch_linear(dt, EPI_LOGITS, m->z, C, m->wte, Bk, m->V, C, el, s);
+  launch_linear(dt, EPI_LOGITS, nullptr, C, &lnf, m->wte, Bk, m->V, C, el, s);
 }
 
 static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
@@ -411,6 +416,11 @@ static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
   a.lens = kv->lens;
   a.limit = kv->limit;
   a.status = m->status;
+  a.wte = m->wte;
+  a.wpe = m->wpe;
+  a.C = m->C;
+  a.dtype = m->cfg.dtype;
+  a.x = m->x;
   return a;
 }
 
@@ -420,9 +430,7 @@ static int capture(ngpt_model* m, GraphSlot& g, const ngpt_kv* kv, int mode,
   hipStream_t s = m->cap;
   HIP_TRY(m, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
   const SamplerArgs a = head_args(m, kv, mode, arg_in, arg_out);
-  launch_sampler(mode, a.logits, a.ld, kv->batch, a.V, a.uniforms, a.params,
-                 a.feed_ids, a.next_ids, a.tok, a.pos, a.lens, a.limit,
-                 a.status, s);
+  launch_sampler(a, kv->batch, s);
   enqueue_decode_forward(m, kv, s);
   hipError_t le = hipGetLastError();
   hipGraph_t graph = nullptr;
@@ -503,9 +511,16 @@ int ngpt_sample(ngpt_model* m, const float* logits, int32_t ld, int32_t B,
   if (B > m->cfg.max_batch) return fail(m, NGPT_E_SIZE, "B > max_batch");
   if (!uniforms && !m->h_params.greedy)
     return fail(m, NGPT_E_ARG, "uniforms is NULL and sampling is not greedy");
-  launch_sampler(SAMPLE_ONLY, logits, ld, B, m->V, uniforms, m->params, nullptr,
-                 next_ids, nullptr, nullptr, nullptr, nullptr, m->status,
-                 m->stream);
+  SamplerArgs a;
+  a.mode = SAMPLE_ONLY;
+  a.logits = logits;
+  a.ld = ld;
+  a.V = m->V;
+  a.uniforms = uniforms;
+  a.params = m->params;
+  a.next_ids = next_ids;
+  a.status = m->status;
+  launch_sampler(a, B, m->stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("sample: ") + hipGetErrorString(e));
   return NGPT_OK;

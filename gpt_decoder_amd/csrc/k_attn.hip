@@ -19,8 +19,8 @@
 //                       softmax in fp32; tiles above the diagonal skipped.
 //   attn_prefill_simt   one thread per query row (fp32 model).
 //   attn_decode         one query per sequence, split over 64-key chunks;
-//                       each workgroup leaves (max, sum, o) and the last one
-//                       to finish merges the chunks in chunk order.
+//                       each workgroup leaves (max, sum, o) for its chunk and
+//                       a second small launch merges the chunks in order.
 #include <math.h>
 
 #include "common.hpp"
@@ -81,28 +81,55 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int last_key = min(q0 + 63, len - 1);
-  for (int k0 = 0; k0 <= last_key; k0 += KT) {
-    __syncthreads();
-    // stage K (key-major) and V (transposed, dim-major); rows past the
-    // sequence are zero so that masked keys contribute exactly nothing
-    constexpr int CH = KT * HS / 8;  // 16-byte chunks per tile
-    for (int c = tid; c < CH; c += 256) {
-      const int key = c / (HS / 8);
-      const int d0 = (c % (HS / 8)) * 8;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (k0 + key < len) {
-        kv4 = *reinterpret_cast<const uint4*>(kbase + (size_t)(k0 + key) * HS + d0);
-        vv4 = *reinterpret_cast<const uint4*>(vbase + (size_t)(k0 + key) * HS + d0);
-      }
-      *reinterpret_cast<uint4*>(sK + key * KS + d0) = kv4;
-      const uint32_t w4[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+  // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
+  // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
+  // The next tile's items are loaded into registers while the current tile
+  // is multiplied.
+  constexpr int ITEMS = (KT / 2) * (HS / 8);
+  constexpr int IPT = (ITEMS + 255) / 256;
+  uint4 rk[IPT][2], rv[IPT][2];
+  auto load_tile = [&](int k0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sVt[(d0 + 2 * j) * VS + key] = static_cast<bf16_t>(w4[j] & 0xFFFFu);
-        sVt[(d0 + 2 * j + 1) * VS + key] = static_cast<bf16_t>(w4[j] >> 16);
+    for (int it = 0; it < IPT; ++it) {
+      const int c = tid + it * 256;
+      const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int key = k0 + 2 * kp + e2;
+        const bool ok = c < ITEMS && key < len;
+        rk[it][e2] = ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * HS + d0)
+                        : make_uint4(0, 0, 0, 0);
+        rv[it][e2] = ok ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * HS + d0)
+                        : make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int c = tid + it * 256;
+      if (c >= ITEMS) break;
+      const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
+      *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rk[it][0];
+      *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rk[it][1];
+      const uint32_t a[4] = {rv[it][0].x, rv[it][0].y, rv[it][0].z, rv[it][0].w};
+      const uint32_t b2[4] = {rv[it][1].x, rv[it][1].y, rv[it][1].z, rv[it][1].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // dims d0+2j (low halves) and d0+2j+1 (high halves) of the two keys
+        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j) * VS + 2 * kp) =
+            (a[j] & 0xFFFFu) | (b2[j] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j + 1) * VS + 2 * kp) =
+            (a[j] >> 16) | (b2[j] & 0xFFFF0000u);
+      }
+    }
+  };
+  load_tile(0);
+  for (int k0 = 0; k0 <= last_key; k0 += KT) {
     __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (k0 + KT <= last_key) load_tile(k0 + KT);
 
     // S^T for 4 sub-tiles of 16 keys
     f32x4_t s[4];
@@ -232,91 +259,76 @@ __global__ __launch_bounds__(64) void attn_prefill_simt(
 // ---------------------------------------------------------------------------
 constexpr int kDecChunk = 64;
 
-__device__ __forceinline__ void merge_state(float& m, float& l, float* o,
-                                            float m2, float l2,
-                                            const float* o2, int n) {
-  const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;
-  const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-  const float c = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
-  l = l * a + l2 * c;
-  for (int j = 0; j < n; ++j) o[j] = o[j] * a + o2[j] * c;
-  m = mn;
-}
-
 template <class T, int HS>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ pos, int H, int Tb, int nchunk, float scale,
-    float* __restrict__ part, int32_t* __restrict__ counters,
-    T* __restrict__ y) {
+    float* __restrict__ part) {
   constexpr int LPK = HS / 8;          // lanes per key
   constexpr int KPP = 64 / LPK;        // keys per wavefront pass
   constexpr int KPW = kDecChunk / 4;   // keys per wavefront
   constexpr int PS = HS + 2;           // partial record: m, l, o[HS]
   __shared__ float sw[4][PS];
-  __shared__ int s_last;
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int C = H * HS;
   const int p = pos[b];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (p < 0) {  // inactive sequence: zero output, no cache access
-    if (chunk == 0 && tid < HS) y[(size_t)b * C + h * HS + tid] = from_f32<T>(0.f);
-    return;
-  }
-  const int nact = p / kDecChunk + 1;  // chunks holding keys 0..p
-  if (chunk >= nact) return;
+  if (p < 0 || chunk > p / kDecChunk) return;  // inactive row / empty chunk
 
   const int sub = lane % LPK;   // which 8 dims
   const int kgrp = lane / LPK;  // key slot within a pass
   const float sl2 = scale * kLog2e;
+  const T* kbase = kc + ((size_t)b * H + h) * Tb * HS;
+  const T* vbase = vc + ((size_t)b * H + h) * Tb * HS;
+
+  // issue every K/V load of this lane first, then the query
+  const int kw = chunk * kDecChunk + wave * KPW;
+  float kf[KPW / KPP][8], vf[KPW / KPP][8];
+#pragma unroll
+  for (int pass = 0; pass < KPW / KPP; ++pass) {
+    const int u = kw + pass * KPP + kgrp;
+    if (u <= p) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kbase + (size_t)u * HS + sub * 8), kf[pass]);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(vbase + (size_t)u * HS + sub * 8), vf[pass]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kf[pass][j] = to_f32(kbase[(size_t)u * HS + sub * 8 + j]);
+          vf[pass][j] = to_f32(vbase[(size_t)u * HS + sub * 8 + j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kf[pass][j] = vf[pass][j] = 0.f;
+    }
+  }
   float qv[8];
   {
     const T* qp = q + (size_t)b * C + h * HS + sub * 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) qv[j] = to_f32(qp[j]) * sl2;
   }
-  const T* kbase = kc + ((size_t)b * H + h) * Tb * HS;
-  const T* vbase = vc + ((size_t)b * H + h) * Tb * HS;
 
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
-
-  const int kw = chunk * kDecChunk + wave * KPW;
 #pragma unroll
   for (int pass = 0; pass < KPW / KPP; ++pass) {
     const int u = kw + pass * KPP + kgrp;
-    const bool valid = u <= p;
-    float kf[8], vf[8];
-    if (valid) {
-      if constexpr (sizeof(T) == 2) {
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kbase + (size_t)u * HS + sub * 8), kf);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(vbase + (size_t)u * HS + sub * 8), vf);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kf[j] = to_f32(kbase[(size_t)u * HS + sub * 8 + j]);
-          vf[j] = to_f32(vbase[(size_t)u * HS + sub * 8 + j]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kf[j] = vf[j] = 0.f;
-    }
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s = fmaf(qv[j], kf[j], s);
+    for (int j = 0; j < 8; ++j) s = fmaf(qv[j], kf[pass][j], s);
 #pragma unroll
     for (int o2 = 1; o2 < LPK; o2 <<= 1) s += __shfl_xor(s, o2, 64);
-    if (valid) {
+    if (u <= p) {
       const float mn = fmaxf(m, s);
       const float a = exp2f(m - mn);  // m = -inf gives 0
       const float pr = exp2f(s - mn);
       l = l * a + pr;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = o[j] * a + pr * vf[j];
+      for (int j = 0; j < 8; ++j) o[j] = o[j] * a + pr * vf[pass][j];
       m = mn;
     }
   }
@@ -349,31 +361,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       rec[1] = ll;
     }
   }
-  // the last workgroup of this (sequence, head) merges all chunks
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(&counters[b * H + h], 1,
-                                            __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == nact - 1);
+}
+
+// Merge the chunk records of one (sequence, head) in chunk order.  Runs as
+// its own launch, so the records of every chunk are visible without fences.
+template <class T, int HS>
+__global__ __launch_bounds__(64) void attn_decode_combine(
+    const float* __restrict__ part, const int32_t* __restrict__ pos, int H,
+    int nchunk, T* __restrict__ y) {
+  constexpr int PS = HS + 2;
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int C = H * HS;
+  const int p = pos[b];
+  if (t >= HS) return;
+  if (p < 0) {  // inactive sequence: a zero row keeps later layers finite
+    y[(size_t)b * C + h * HS + t] = from_f32<T>(0.f);
+    return;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid < HS) {
-    const float* base = part + ((size_t)b * H + h) * nchunk * PS;
-    float mm = -INFINITY, ll = 0.f, oo = 0.f;
-    for (int c = 0; c < nact; ++c) {
-      const float* r = base + (size_t)c * PS;
-      const float rm = __hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float rl = __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float ro = __hip_atomic_load(r + 2 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      merge_state(mm, ll, &oo, rm, rl, &ro, 1);
+  const int nact = p / kDecChunk + 1;
+  const float* base = part + ((size_t)b * H + h) * nchunk * PS;
+  float mm = -INFINITY, ll = 0.f, oo = 0.f;
+  for (int c0 = 0; c0 < nact; c0 += 8) {
+    float rm[8], rl[8], ro[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* r = base + (size_t)(c0 + u) * PS;
+      const bool ok = c0 + u < nact;
+      rm[u] = ok ? r[0] : -INFINITY;
+      rl[u] = ok ? r[1] : 0.f;
+      ro[u] = ok ? r[2 + t] : 0.f;
     }
-    y[(size_t)b * C + h * HS + tid] = from_f32<T>(oo / ll);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) merge_state(mm, ll, &oo, rm[u], rl[u], &ro[u], 1);
   }
-  if (tid == 0) counters[b * H + h] = 0;
+  y[(size_t)b * C + h * HS + t] = from_f32<T>(oo / ll);
 }
 
 // ---------------------------------------------------------------------------
@@ -403,31 +424,35 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
 
 int attn_decode_chunks(int Tb) { return (Tb + kDecChunk - 1) / kDecChunk; }
 
+int attn_decode_chunk_keys() { return kDecChunk; }
+
 void launch_attn_decode(int dtype, const void* q, const void* kc,
                         const void* vc, const int32_t* pos, int B, int H,
-                        int hs, int Tb, float* part, int32_t* counters,
-                        void* y, hipStream_t s) {
+                        int hs, int Tb, float* part, void* y,
+                        bool merge_into_y, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hs);
   const int nchunk = attn_decode_chunks(Tb);
-  const dim3 grid(nchunk, H, B);
+  const dim3 grid(nchunk, H, B), cgrid(H, B);
   if (dtype == NGPT_BF16) {
-    if (hs == 64)
+    if (hs == 64) {
       attn_decode_kernel<bf16_t, 64><<<grid, 256, 0, s>>>((const bf16_t*)q,
-          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part,
-          counters, (bf16_t*)y);
-    else
+          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part);
+      if (merge_into_y) attn_decode_combine<bf16_t, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (bf16_t*)y);
+    } else {
       attn_decode_kernel<bf16_t, 32><<<grid, 256, 0, s>>>((const bf16_t*)q,
-          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part,
-          counters, (bf16_t*)y);
+          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part);
+      if (merge_into_y) attn_decode_combine<bf16_t, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (bf16_t*)y);
+    }
   } else {
-    if (hs == 64)
+    if (hs == 64) {
       attn_decode_kernel<float, 64><<<grid, 256, 0, s>>>((const float*)q,
-          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part,
-          counters, (float*)y);
-    else
+          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part);
+      if (merge_into_y) attn_decode_combine<float, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (float*)y);
+    } else {
       attn_decode_kernel<float, 32><<<grid, 256, 0, s>>>((const float*)q,
-          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part,
-          counters, (float*)y);
+          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part);
+      if (merge_into_y) attn_decode_combine<float, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (float*)y);
+    }
   }
 }
 

@@ -68,7 +68,11 @@ __global__ __launch_bounds__(256) void embed_decode_kernel(
     xr[c] = to_f32(te[c]) + to_f32(pe[c]);
 }
 
-// One wavefront per row; 4 rows per 256-thread block.
+// One wavefront per row; 4 rows per 256-thread block.  The row is held in
+// registers (float4 per lane per 256 columns, up to 8 of them), so x is read
+// once and every load is issued before the first reduction.
+constexpr int kLnMaxVec = 8;  // C <= 2048
+
 template <class T>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const float* __restrict__ x, int ldx, const int32_t* __restrict__ rows,
@@ -79,21 +83,39 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   if (i >= M) return;
   const int src = rows ? rows[i] : i;
   const float* xr = x + (size_t)src * ldx;
+  float4 v[kLnMaxVec];
   float s = 0.f;
-  for (int c = lane; c < C; c += 64) s += xr[c];
-  const float mean = wave_sum(s) / (float)C;
-  float v = 0.f;
-  for (int c = lane; c < C; c += 64) {
-    const float d = xr[c] - mean;
-    v += d * d;
+#pragma unroll
+  for (int j = 0; j < kLnMaxVec; ++j) {
+    const int c = j * 256 + lane * 4;
+    v[j] = c < C ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float var = wave_sum(v) / (float)C;
-  const float rstd = 1.0f / sqrtf(var + 1e-5f);
+#pragma unroll
+  for (int j = 0; j < kLnMaxVec; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  const float mean = wave_sum(s) / (float)C;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnMaxVec; ++j) {
+    const int c = j * 256 + lane * 4;
+    if (c < C) {
+      const float a = v[j].x - mean, b = v[j].y - mean, d = v[j].z - mean, e = v[j].w - mean;
+      q += (a * a + b * b) + (d * d + e * e);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)C + 1e-5f);
   T* o = out + (size_t)i * ldo;
-  for (int c = lane; c < C; c += 64) {
-    float y = (xr[c] - mean) * rstd * to_f32(w[c]);
-    if (bias) y += to_f32(bias[c]);
-    o[c] = from_f32<T>(y);
+#pragma unroll
+  for (int j = 0; j < kLnMaxVec; ++j) {
+    const int c = j * 256 + lane * 4;
+    if (c < C) {
+      const float xv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float y = (xv[u] - mean) * rstd * to_f32(w[c + u]);
+        if (bias) y += to_f32(bias[c + u]);
+        o[c + u] = from_f32<T>(y);
+      }
+    }
   }
 }
 

@@ -12,14 +12,16 @@
 // Kernels:
 //   gemm_mfma_kernel  bf16 MFMA (v_mfma_f32_16x16x32_bf16) tile GEMM for
 //                     many rows (prefill, batched decode);
-//   gemv_kernel       streaming matrix-vector kernel for a few rows (decode),
-//                     bandwidth-bound: 16-byte weight loads, one wavefront per
-//                     output column;
+//   gemv_kernel       streaming matrix-vector kernel for up to 4 rows (decode),
+//                     bandwidth-bound: 16-byte weight loads issued ahead of the
+//                     activations, optional fused LayerNorm prologue;
 //   gemm_f32_kernel   fp32 tiled kernel (the fp32 model).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace ngpt {
+
+constexpr int kGemvMaxRows = 4;  // rows handled by the streaming kernels
 
 template <class T, int EPI>
 __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
@@ -58,8 +60,14 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
 // ---------------------------------------------------------------------------
 // bf16 MFMA tile GEMM.  256 threads = 4 wavefronts in a 2x2 arrangement; each
 // wavefront owns a (BM/2) x (BN/2) sub-tile built from 16x16 MFMA tiles.  K is
-// consumed 64 at a time: the next K-slab is fetched into registers while the
-// current one is multiplied out of LDS.
+// consumed 64 at a time through a two-stage LDS ring: the next K-slab is
+// fetched into registers while the current one is multiplied, then written
+// to the other LDS stage, so one barrier per K-slab suffices.
+//
+// Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs,
+// so tile t goes to the workgroup that lands on XCD t / (tiles / 8); each XCD
+// then walks its tiles with the row-block index fastest, and tiles sharing a
+// weight panel run back to back on the same L2.
 //
 // MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l supplies row
 // (l % 16) of A and column (l % 16) of B, each as 8 consecutive K values
@@ -77,15 +85,19 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread (A tile)
   constexpr int BCH = BN * 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[BM * LDS];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[BN * LDS];
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int mt = (M + BM - 1) / BM;
+  const int ntile = gridDim.x;
+  int t = blockIdx.x;
+  if ((ntile & 7) == 0) t = (t & 7) * (ntile >> 3) + (t >> 3);
+  const int m0 = (t % mt) * BM;
+  const int n0 = (t / mt) * BN;
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -112,37 +124,38 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
                       : make_uint4(0, 0, 0, 0);
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int st) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(sA + (c >> 3) * LDS + (c & 7) * 8) = ra[i];
+      *reinterpret_cast<uint4*>(sA[st] + (c >> 3) * LDS + (c & 7) * 8) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(sB + (c >> 3) * LDS + (c & 7) * 8) = rb[i];
+      *reinterpret_cast<uint4*>(sB[st] + (c >> 3) * LDS + (c & 7) * 8) = rb[i];
     }
   };
 
+  const int nk = K / BK;
   gload(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (k0 + BK < K) gload(k0 + BK);
+  sstore(0);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int st = it & 1;
+    if (it + 1 < nk) gload((it + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sA + r * LDS + kk + (lane >> 4) * 8);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sA[st] + r * LDS + kk + (lane >> 4) * 8);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * WN + j * 16 + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB + r * LDS + kk + (lane >> 4) * 8);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB[st] + r * LDS + kk + (lane >> 4) * 8);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -151,6 +164,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
                                                               acc[i][j], 0, 0, 0);
     }
+    if (it + 1 < nk) sstore(st ^ 1);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -168,53 +183,336 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Streaming GEMV for M <= MR rows: one wavefront per output column n reads the
-// weight row W[n][:] once with 16-byte loads and multiplies it with every A
-// row; a wavefront-wide reduction finishes each dot product.
+// Streaming GEMV for M <= MR (1, 2 or 4) rows, one wavefront per workgroup.
+// A wavefront owns CPW consecutive output columns; lane l multiplies the
+// K-elements l*VE .. l*VE+VE-1 of each 64*VE-wide chunk.  Every chunk's
+// weight loads (16 bytes per lane per column) are issued before the
+// activations are touched, so the weight stream is in flight while the
+// activation rows (and their LayerNorm statistics) arrive.
+//
+// With LN, the A rows are LN(x) computed here from the fp32 residual x:
+// each lane normalises exactly the elements it multiplies, and rounds them to
+// the model dtype as the bf16 data path stores its LayerNorm output.
 // ---------------------------------------------------------------------------
-template <class T, int EPI, int MR>
-__global__ __launch_bounds__(256) void gemv_kernel(
-    const T* __restrict__ A, int lda, const T* __restrict__ W, int M, int N,
-    int K, EpiArgs e) {
-  constexpr int VE = 16 / sizeof(T);
+
+// Sum R = 2^LG values across the wavefront.  Returns the sum of value index
+// (lane >> (6 - LG)) in lanes whose low (6 - LG) bits are zero.
+template <int LG>
+__device__ __forceinline__ float wave_reduce_multi(float* v) {
+  constexpr int R = 1 << LG;
   const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  float acc[MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-  const T* wr = W + (size_t)n * K;
-  for (int k = lane * VE; k < K; k += 64 * VE) {
-    float wf[VE];
-    if constexpr (sizeof(T) == 2) {
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(wr + k), wf);
-    } else {
-      const float4 t = *reinterpret_cast<const float4*>(wr + k);
-      wf[0] = t.x; wf[1] = t.y; wf[2] = t.z; wf[3] = t.w;
+  for (int st = 0; st < LG; ++st) {
+    const int o = 32 >> st;
+    const int cnt = R >> st;
+    const bool hi = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < cnt / 2; ++i) {
+      const float send = hi ? v[i] : v[i + cnt / 2];
+      const float keep = hi ? v[i + cnt / 2] : v[i];
+      v[i] = keep + __shfl_xor(send, o, 64);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int o = 32 >> LG; o > 0; o >>= 1) r += __shfl_xor(r, o, 64);
+  return r;
+}
+
+__device__ __forceinline__ void load_vec(const bf16_t* p, float* f) {
+  bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
+}
+__device__ __forceinline__ void load_vec(const float* p, float* f) {
+  const float4 t = *reinterpret_cast<const float4*>(p);
+  f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+}
+template <class T>
+__device__ __forceinline__ float round_to(float v) {
+  return to_f32(from_f32<T>(v));
+}
+
+template <class T, int EPI, int MR, int CPW, int NCH, bool LN>
+__global__ __launch_bounds__(64) void gemv_kernel(
+    const T* __restrict__ A, int lda, LnArgs ln, const T* __restrict__ W,
+    int M, int N, int K, EpiArgs e) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int SPAN = 64 * VE;
+  constexpr int LG = (MR * CPW == 1) ? 0 : (MR * CPW == 2) ? 1
+                   : (MR * CPW == 4) ? 2 : (MR * CPW == 8) ? 3 : 4;
+  static_assert((1 << LG) == MR * CPW, "MR*CPW must be a power of two <= 16");
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * CPW;
+
+  // 1. every load of this lane, issued before any of them is used
+  uint4 wv[NCH][CPW];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int k = j * SPAN + lane * VE;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int n = min(n0 + c, N - 1);
+      wv[j][c] = (k < K) ? *reinterpret_cast<const uint4*>(W + (size_t)n * K + k)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // A rows: LN keeps the raw fp32 x values (normalised below); otherwise the
+  // packed 16-byte vectors are kept and widened at use
+  float av[LN ? MR : 1][LN ? NCH : 1][VE];
+  uint4 araw[LN ? 1 : MR][LN ? 1 : NCH];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int k = j * SPAN + lane * VE;
+      const bool ok = m < M && k < K;
+      if constexpr (LN) {
+        const float* xr = ln.x + (size_t)m * ln.ldx + k;
+#pragma unroll
+        for (int q = 0; q < VE; q += 4) {
+          const float4 t4 = ok ? *reinterpret_cast<const float4*>(xr + q)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+          av[m][j][q] = t4.x; av[m][j][q + 1] = t4.y;
+          av[m][j][q + 2] = t4.z; av[m][j][q + 3] = t4.w;
+        }
+      } else {
+        araw[m][j] = ok ? *reinterpret_cast<const uint4*>(A + (size_t)m * lda + k)
+                        : make_uint4(0, 0, 0, 0);
+      }
+    }
+
+  // 2. LayerNorm of the A rows (two-pass statistics over the K features)
+  if constexpr (LN) {
+    float g[NCH][VE], bb[NCH][VE];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int k = j * SPAN + lane * VE;
+      if (k < K) {
+        load_vec(static_cast<const T*>(ln.w) + k, g[j]);
+        if (ln.b) load_vec(static_cast<const T*>(ln.b) + k, bb[j]);
+        else {
+#pragma unroll
+          for (int q = 0; q < VE; ++q) bb[j][q] = 0.f;
+        }
+      }
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      if (m < M) {
-        float af[VE];
-        if constexpr (sizeof(T) == 2) {
-          bf16x8_to_f32(*reinterpret_cast<const uint4*>(A + (size_t)m * lda + k), af);
-        } else {
-          const float4 t = *reinterpret_cast<const float4*>(A + (size_t)m * lda + k);
-          af[0] = t.x; af[1] = t.y; af[2] = t.z; af[3] = t.w;
-        }
+      float sm = 0.f;
 #pragma unroll
-        for (int q = 0; q < VE; ++q) acc[m] = fmaf(af[q], wf[q], acc[m]);
+      for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int q = 0; q < VE; ++q) sm += av[m][j][q];
+      const float mu = wave_sum(sm) / (float)K;
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int k = j * SPAN + lane * VE;
+        if (k < K) {
+#pragma unroll
+          for (int q = 0; q < VE; ++q) {
+            const float d = av[m][j][q] - mu;
+            sq += d * d;
+          }
+        }
+      }
+      const float rs = 1.0f / sqrtf(wave_sum(sq) / (float)K + 1e-5f);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int k = j * SPAN + lane * VE;
+#pragma unroll
+        for (int q = 0; q < VE; ++q)
+          av[m][j][q] = (k < K) ? round_to<T>((av[m][j][q] - mu) * rs * g[j][q] + bb[j][q]) : 0.f;
       }
     }
   }
+
+  // 3. dot products
+  float acc[MR * CPW];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = wave_sum(acc[m]);
-  if (lane == 0) {
+  for (int i = 0; i < MR * CPW; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
-      if (m < M) epi_apply<T, EPI>(e, m, n, acc[m]);
+  for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      float wf[VE];
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_to_f32(wv[j][c], wf);
+      } else {
+        wf[0] = __uint_as_float(wv[j][c].x);
+        wf[1] = __uint_as_float(wv[j][c].y);
+        wf[2] = __uint_as_float(wv[j][c].z);
+        wf[3] = __uint_as_float(wv[j][c].w);
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float af[VE];
+        if constexpr (LN) {
+#pragma unroll
+          for (int q = 0; q < VE; ++q) af[q] = av[m][j][q];
+        } else if constexpr (sizeof(T) == 2) {
+          bf16x8_to_f32(araw[m][j], af);
+        } else {
+          af[0] = __uint_as_float(araw[m][j].x);
+          af[1] = __uint_as_float(araw[m][j].y);
+          af[2] = __uint_as_float(araw[m][j].z);
+          af[3] = __uint_as_float(araw[m][j].w);
+        }
+#pragma unroll
+        for (int q = 0; q < VE; ++q)
+          acc[m * CPW + c] = fmaf(af[q], wf[q], acc[m * CPW + c]);
+      }
+    }
+  }
+
+  const float r = wave_reduce_multi<LG>(acc);
+  constexpr int LOW = (1 << (6 - LG)) - 1;
+  if ((lane & LOW) == 0) {
+    const int idx = lane >> (6 - LG);
+    const int m = idx / CPW, c = idx % CPW;
+    const int n = n0 + c;
+    if (m < M && n < N) epi_apply<T, EPI>(e, m, n, r);
   }
 }
+
+// ---------------------------------------------------------------------------
+// Decode output projection with the attention chunk merge folded in:
+//   y[m] = merge over key chunks of the split-K attention records,
+//   x[m] += y[m] W_proj^T + b.
+// 256 threads; each wavefront owns 4 output columns.  Weight loads are issued
+// first; the merge of every (row, head, dim) item then fills an LDS copy of
+// y (rounded to the model dtype, as the attention output is stored), records
+// merged in chunk order with eight records' loads in flight at a time.
+// ---------------------------------------------------------------------------
+constexpr int kProjCols = 16;       // output columns per workgroup
+constexpr int kProjMaxK = 2048;     // n_embd bound
+
+template <class T, int HS, int MR, int NCH>
+__global__ __launch_bounds__(256) void attn_proj_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ pos, int H,
+    int nchunk, int chunk_keys, const T* __restrict__ W, int M, int N, int K,
+    EpiArgs e) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int SPAN = 64 * VE;
+  constexpr int CPW = 4;
+  constexpr int PS = HS + 2;
+  constexpr int LG = (MR * CPW == 4) ? 2 : (MR * CPW == 8) ? 3 : 4;
+  __shared__ __attribute__((aligned(16))) float sy[MR][kProjMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * kProjCols + wave * CPW;
+
+  uint4 wv[NCH][CPW];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int k = j * SPAN + lane * VE;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int n = min(n0 + c, N - 1);
+      wv[j][c] = (k < K) ? *reinterpret_cast<const uint4*>(W + (size_t)n * K + k)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  for (int it = tid; it < M * K; it += 256) {
+    const int m = it / K, f = it - m * K;
+    const int h = f / HS, d = f - h * HS;
+    const int p = pos[m];
+    float yv = 0.f;
+    if (p >= 0) {
+      const int nact = p / chunk_keys + 1;
+      const float* base = part + ((size_t)m * H + h) * nchunk * PS;
+      float mm = -INFINITY, ll = 0.f, oo = 0.f;
+      for (int c0 = 0; c0 < nact; c0 += 8) {
+        float rm[8], rl[8], ro[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float* r = base + (size_t)(c0 + u) * PS;
+          const bool ok = c0 + u < nact;
+          rm[u] = ok ? r[0] : -INFINITY;
+          rl[u] = ok ? r[1] : 0.f;
+          ro[u] = ok ? r[2 + d] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) merge_state(mm, ll, &oo, rm[u], rl[u], &ro[u], 1);
+      }
+      yv = round_to<T>(oo / ll);
+    }
+    sy[m][f] = yv;
+  }
+  __syncthreads();
+
+  float acc[MR * CPW];
+#pragma unroll
+  for (int i = 0; i < MR * CPW; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int k = j * SPAN + lane * VE;
+    if (k >= K) break;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      float wf[VE];
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_to_f32(wv[j][c], wf);
+      } else {
+        wf[0] = __uint_as_float(wv[j][c].x);
+        wf[1] = __uint_as_float(wv[j][c].y);
+        wf[2] = __uint_as_float(wv[j][c].z);
+        wf[3] = __uint_as_float(wv[j][c].w);
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int q = 0; q < VE; ++q)
+          acc[m * CPW + c] = fmaf(sy[m][k + q], wf[q], acc[m * CPW + c]);
+    }
+  }
+  const float r = wave_reduce_multi<LG>(acc);
+  constexpr int LOW = (1 << (6 - LG)) - 1;
+  if ((lane & LOW) == 0) {
+    const int idx = lane >> (6 - LG);
+    const int m = idx / CPW, c = idx % CPW;
+    const int n = n0 + c;
+    if (m < M && n < N) epi_apply<T, EPI_RESID>(e, m, n, r);
+  }
+}
+
+template <class T, int HS, int MR>
+static void launch_attn_proj_t(const float* part, const int32_t* pos, int H,
+                               int nchunk, int chunk_keys, const T* W, int M,
+                               int N, int K, const EpiArgs& e, hipStream_t s) {
+  constexpr int SPAN = 64 * (16 / sizeof(T));
+  const int grid = (N + kProjCols - 1) / kProjCols;
+  if (K <= 2 * SPAN)
+    attn_proj_kernel<T, HS, MR, 2><<<grid, 256, 0, s>>>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e);
+  else if (K <= 4 * SPAN)
+    attn_proj_kernel<T, HS, MR, 4><<<grid, 256, 0, s>>>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e);
+  else
+    attn_proj_kernel<T, HS, MR, 8><<<grid, 256, 0, s>>>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e);
+}
+
+template <class T, int HS>
+static void launch_attn_proj_h(const float* part, const int32_t* pos, int H,
+                               int nchunk, int chunk_keys, const T* W, int M,
+                               int N, int K, const EpiArgs& e, hipStream_t s) {
+  if (M <= 1) launch_attn_proj_t<T, HS, 1>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e, s);
+  else if (M <= 2) launch_attn_proj_t<T, HS, 2>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e, s);
+  else launch_attn_proj_t<T, HS, 4>(part, pos, H, nchunk, chunk_keys, W, M, N, K, e, s);
+}
+
+void launch_attn_proj(int dtype, const float* part, const int32_t* pos, int H,
+                      int hs, int nchunk, int chunk_keys, const void* W, int M,
+                      int C, const EpiArgs& e, hipStream_t s) {
+  if (dtype == NGPT_BF16) {
+    const bf16_t* w = static_cast<const bf16_t*>(W);
+    if (hs == 64) launch_attn_proj_h<bf16_t, 64>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+    else launch_attn_proj_h<bf16_t, 32>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+  } else {
+    const float* w = static_cast<const float*>(W);
+    if (hs == 64) launch_attn_proj_h<float, 64>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+    else launch_attn_proj_h<float, 32>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+  }
+}
+
+bool decode_fused_proj(int M) { return M <= kGemvMaxRows; }
 
 // ---------------------------------------------------------------------------
 // fp32 tiled GEMM, 16x16 outputs per 256-thread block.
@@ -242,48 +540,99 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+template <class T, int EPI, int MR, int CPW, bool LN>
+static void launch_gemv_c(const T* A, int lda, const LnArgs& ln, const T* W,
+                          int M, int N, int K, const EpiArgs& e, hipStream_t s) {
+  constexpr int SPAN = 64 * (16 / sizeof(T));
+  const int nch = (K + SPAN - 1) / SPAN;
+  const int grid = (N + CPW - 1) / CPW;
+  if (nch <= 2)
+    gemv_kernel<T, EPI, MR, CPW, 2, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+  else if (nch <= 4)
+    gemv_kernel<T, EPI, MR, CPW, 4, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+  else if (nch <= 8)
+    gemv_kernel<T, EPI, MR, CPW, 8, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+  else
+    gemv_kernel<T, EPI, MR, CPW, 16, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+}
+
+template <class T, int EPI, int MR, bool LN>
+static void launch_gemv(const T* A, int lda, const LnArgs& ln, const T* W,
+                        int M, int N, int K, const EpiArgs& e, hipStream_t s) {
+  // enough wavefronts to cover every CU several times over; more columns per
+  // wavefront only where the weight rows are short
+  constexpr int SPAN = 64 * (16 / sizeof(T));
+  const int nch = (K + SPAN - 1) / SPAN;
+  if (N >= 16384 && MR == 1 && nch <= 4)
+    launch_gemv_c<T, EPI, MR, 4, LN>(A, lda, ln, W, M, N, K, e, s);
+  else if (N >= 2048 && MR <= 2 && nch <= 4)
+    launch_gemv_c<T, EPI, MR, 2, LN>(A, lda, ln, W, M, N, K, e, s);
+  else
+    launch_gemv_c<T, EPI, MR, 1, LN>(A, lda, ln, W, M, N, K, e, s);
+}
+
+template <class T, int EPI, bool LN>
+static void gemv_rows(const T* A, int lda, const LnArgs& ln, const T* W, int M,
+                      int N, int K, const EpiArgs& e, hipStream_t s) {
+  if (M <= 1) launch_gemv<T, EPI, 1, LN>(A, lda, ln, W, M, N, K, e, s);
+  else if (M <= 2) launch_gemv<T, EPI, 2, LN>(A, lda, ln, W, M, N, K, e, s);
+  else launch_gemv<T, EPI, 4, LN>(A, lda, ln, W, M, N, K, e, s);
+}
+
+
 template <int EPI>
-static void dispatch(int dtype, const void* A, int lda, const void* W, int M,
-                     int N, int K, const EpiArgs& e, hipStream_t s) {
+static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
+                     const void* W, int M, int N, int K, const EpiArgs& e,
+                     hipStream_t s) {
+  const LnArgs none{};
+  if (M <= kGemvMaxRows) {
+    if (dtype == NGPT_BF16) {
+      const bf16_t* a = static_cast<const bf16_t*>(A);
+      const bf16_t* w = static_cast<const bf16_t*>(W);
+      if (ln) gemv_rows<bf16_t, EPI, true>(a, lda, *ln, w, M, N, K, e, s);
+      else gemv_rows<bf16_t, EPI, false>(a, lda, none, w, M, N, K, e, s);
+    } else {
+      const float* a = static_cast<const float*>(A);
+      const float* w = static_cast<const float*>(W);
+      if (ln) gemv_rows<float, EPI, true>(a, lda, *ln, w, M, N, K, e, s);
+      else gemv_rows<float, EPI, false>(a, lda, none, w, M, N, K, e, s);
+    }
+    return;
+  }
+  if (ln) {  // tiled paths read a materialised LayerNorm output
+    launch_layernorm(dtype, ln->x, ln->ldx, nullptr, M, ln->w, ln->b, ln->h, K, K, s);
+    A = ln->h;
+    lda = K;
+  }
   if (dtype == NGPT_BF16) {
     const bf16_t* a = static_cast<const bf16_t*>(A);
     const bf16_t* w = static_cast<const bf16_t*>(W);
-    if (M <= 8) {
-      const dim3 grid((N + 3) / 4);
-      if (M <= 1)      gemv_kernel<bf16_t, EPI, 1><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else if (M <= 2) gemv_kernel<bf16_t, EPI, 2><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else if (M <= 4) gemv_kernel<bf16_t, EPI, 4><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else             gemv_kernel<bf16_t, EPI, 8><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    } else if (M <= 64) {
-      const dim3 grid((N + 63) / 64, (M + 63) / 64);
-      gemm_mfma_kernel<64, 64, EPI><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    } else {
-      const dim3 grid((N + 127) / 128, (M + 127) / 128);
-      gemm_mfma_kernel<128, 128, EPI><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    }
+    // largest tile that still gives every CU at least one workgroup
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    constexpr int kCUs = 256;
+    if (M > 64 && tiles(128, 128) >= kCUs)
+      gemm_mfma_kernel<128, 128, EPI><<<tiles(128, 128), 256, 0, s>>>(a, lda, w, M, N, K, e);
+    else if (M > 64 && tiles(128, 64) >= kCUs)
+      gemm_mfma_kernel<128, 64, EPI><<<tiles(128, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
+    else
+      gemm_mfma_kernel<64, 64, EPI><<<tiles(64, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
   } else {
-    const float* a = static_cast<const float*>(A);
-    const float* w = static_cast<const float*>(W);
-    if (M <= 4) {
-      const dim3 grid((N + 3) / 4);
-      if (M <= 1) gemv_kernel<float, EPI, 1><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else        gemv_kernel<float, EPI, 4><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    } else {
-      const dim3 grid((N + 15) / 16, (M + 15) / 16);
-      gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    }
+    const dim3 grid((N + 15) / 16, (M + 15) / 16);
+    gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(static_cast<const float*>(A), lda,
+        static_cast<const float*>(W), M, N, K, e);
   }
 }
 
-void launch_linear(int dtype, int epi, const void* A, int lda, const void* W,
-                   int M, int N, int K, const EpiArgs& e, hipStream_t s) {
+void launch_linear(int dtype, int epi, const void* A, int lda,
+                   const LnArgs* ln, const void* W, int M, int N, int K,
+                   const EpiArgs& e, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   switch (epi) {
-    case EPI_STORE: dispatch<EPI_STORE>(dtype, A, lda, W, M, N, K, e, s); break;
-    case EPI_GELU: dispatch<EPI_GELU>(dtype, A, lda, W, M, N, K, e, s); break;
-    case EPI_RESID: dispatch<EPI_RESID>(dtype, A, lda, W, M, N, K, e, s); break;
-    case EPI_QKV: dispatch<EPI_QKV>(dtype, A, lda, W, M, N, K, e, s); break;
-    default: dispatch<EPI_LOGITS>(dtype, A, lda, W, M, N, K, e, s); break;
+    case EPI_STORE: dispatch<EPI_STORE>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    case EPI_GELU: dispatch<EPI_GELU>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    case EPI_RESID: dispatch<EPI_RESID>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    case EPI_QKV: dispatch<EPI_QKV>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    default: dispatch<EPI_LOGITS>(dtype, A, lda, ln, W, M, N, K, e, s); break;
   }
 }
 

@@ -77,13 +77,38 @@ __device__ __forceinline__ float block_max_f(float v, SampShared& sh) {
   return t;
 }
 
-// Greedy: argmax of the raw logits, lowest id among equal maxima.
+// Greedy: argmax of the raw logits, lowest id among equal maxima.  Each
+// thread scans its ids in ascending order, so a strict comparison keeps the
+// first of equal values.
 __device__ int row_argmax(const float* lg, int V, SampShared& sh) {
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int i = threadIdx.x; i < V; i += kSampThreads) {
+  int tail = 0;
+  if ((reinterpret_cast<uintptr_t>(lg) & 15u) == 0) {
+    const float4* l4 = reinterpret_cast<const float4*>(lg);
+    const int V4 = V >> 2;
+    constexpr int U = 8;  // loads in flight per thread
+    for (int i0 = threadIdx.x; i0 < V4; i0 += U * kSampThreads) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kSampThreads;
+        v[u] = i < V4 ? l4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kSampThreads;
+        if (v[u].x > best) { best = v[u].x; bi = 4 * i; }
+        if (v[u].y > best) { best = v[u].y; bi = 4 * i + 1; }
+        if (v[u].z > best) { best = v[u].z; bi = 4 * i + 2; }
+        if (v[u].w > best) { best = v[u].w; bi = 4 * i + 3; }
+      }
+    }
+    tail = V4 << 2;
+  }
+  for (int i = tail + threadIdx.x; i < V; i += kSampThreads) {
     const float v = lg[i];
-    if (v > best) { best = v; bi = i; }   // ascending i: first max wins
+    if (v > best) { best = v; bi = i; }
   }
   const float gmax = block_max_f(best, sh);
   int cand = (best == gmax) ? bi : 0x7FFFFFFF;
@@ -179,13 +204,23 @@ __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
   return sh.found != 0x7FFFFFFF ? sh.found : sh.last_kept;
 }
 
+template <class T>
+__device__ void write_embedding(const T* wte, const T* wpe, int id, int p,
+                                int C, float* xr) {
+  const T* te = wte + (size_t)id * C;
+  const T* pe = wpe + (size_t)p * C;
+  for (int c = threadIdx.x; c < C; c += blockDim.x)
+    xr[c] = to_f32(te[c]) + to_f32(pe[c]);
+}
+
 __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     int mode, const float* __restrict__ logits, int ld, int V,
     const double* __restrict__ uniforms, const SampleParams* __restrict__ prm,
     const int32_t* __restrict__ feed_ids, int32_t* __restrict__ next_ids,
     int32_t* __restrict__ tok, int32_t* __restrict__ pos,
     int32_t* __restrict__ lens, const int32_t* __restrict__ limit,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, const void* __restrict__ wte,
+    const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x) {
   __shared__ SampShared sh;
   const int b = blockIdx.x;
   bool active = true;
@@ -199,6 +234,8 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
       if (next_ids) next_ids[b] = -1;
       pos[b] = -1;
     }
+    // inactive row: keep its residual finite; nothing of it is stored
+    for (int c = threadIdx.x; c < C; c += blockDim.x) x[(size_t)b * C + c] = 0.f;
     return;
   }
   int id;
@@ -224,31 +261,35 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
       lens[b] = len + 1;
     }
   }
+  if (mode != SAMPLE_ONLY) {
+    float* xr = x + (size_t)b * C;
+    if (dtype == NGPT_BF16)
+      write_embedding((const bf16_t*)wte, (const bf16_t*)wpe, id, len, C, xr);
+    else
+      write_embedding((const float*)wte, (const float*)wpe, id, len, C, xr);
+  }
 }
 
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p) {
-  void* vals[13] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
+  void* vals[18] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
                     &a.feed_ids, &a.next_ids, &a.tok, &a.pos, &a.lens,
-                    &a.limit, &a.status};
-  for (int i = 0; i < 13; ++i) a.ptrs[i] = vals[i];
+                    &a.limit, &a.status, &a.wte, &a.wpe, &a.C, &a.dtype, &a.x};
+  for (int i = 0; i < 18; ++i) a.ptrs[i] = vals[i];
   p->func = reinterpret_cast<void*>(sampler_kernel);
   p->gridDim = dim3(B);
-  p->blockDim = dim3(a.mode == FEED_STEP ? 64 : kSampThreads);
+  p->blockDim = dim3(a.mode == FEED_STEP ? 256 : kSampThreads);
   p->sharedMemBytes = 0;
   p->kernelParams = a.ptrs;
   p->extra = nullptr;
 }
 
-void launch_sampler(int mode, const float* logits, int ld, int B, int V,
-                    const double* uniforms, const SampleParams* params,
-                    const int32_t* feed_ids, int32_t* next_ids, int32_t* tok,
-                    int32_t* pos, int32_t* lens, const int32_t* limit,
-                    int32_t* status, hipStream_t s) {
+void launch_sampler(const SamplerArgs& a, int B, hipStream_t s) {
   if (B <= 0) return;
-  const int threads = (mode == FEED_STEP) ? 64 : kSampThreads;
-  sampler_kernel<<<B, threads, 0, s>>>(mode, logits, ld, V, uniforms, params,
-                                       feed_ids, next_ids, tok, pos, lens,
-                                       limit, status);
+  const int threads = (a.mode == FEED_STEP) ? 256 : kSampThreads;
+  sampler_kernel<<<B, threads, 0, s>>>(a.mode, a.logits, a.ld, a.V, a.uniforms,
+                                       a.params, a.feed_ids, a.next_ids, a.tok,
+                                       a.pos, a.lens, a.limit, a.status, a.wte,
+                                       a.wpe, a.C, a.dtype, a.x);
 }
 
 }  // namespace ngpt

@@ -65,9 +65,22 @@ void launch_layernorm(int dtype, const float* x, int ldx, const int32_t* rows,
                       int M, const void* w, const void* b, void* out, int ldo,
                       int C, hipStream_t s);
 
-// acc = A[M][K] W[N][K]^T, then the epilogue.  A and W are dtype.
-void launch_linear(int dtype, int epi, const void* A, int lda, const void* W,
-                   int M, int N, int K, const EpiArgs& e, hipStream_t s);
+// Optional LayerNorm of the A operand: A = LN(x) with x fp32 [M][ldx] and
+// K = C features.  Paths that need a materialised LN output write it to h
+// ([M][K], dtype) first.
+struct LnArgs {
+  const float* x = nullptr;
+  int ldx = 0;
+  const void* w = nullptr;
+  const void* b = nullptr;
+  void* h = nullptr;
+};
+
+// acc = A[M][K] W[N][K]^T, then the epilogue.  A and W are dtype.  With
+// ln != null the A operand is LN(ln->x) and `A` is ignored.
+void launch_linear(int dtype, int epi, const void* A, int lda,
+                   const LnArgs* ln, const void* W, int M, int N, int K,
+                   const EpiArgs& e, hipStream_t s);
 
 // Causal attention of each packed prefill row against its own sequence's
 // keys in the cache (positions 0..pos).  q is [M][ldq] (head j at columns
@@ -77,12 +90,23 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
                          int hs, int Tb, void* y, int ldy, hipStream_t s);
 
 // One query per active sequence (pos[b] >= 0) against cache rows
-// 0..pos[b], split over key chunks with a cross-workgroup combine.
+// 0..pos[b], split over key chunks: each chunk leaves a record (max, sum,
+// o[hs]) in `part` [B][H][nchunk][hs+2].  With merge_into_y the records are
+// merged (in chunk order) into y [B][C] by a second launch; otherwise the
+// consumer merges them (launch_attn_proj).
 int attn_decode_chunks(int Tb);
+int attn_decode_chunk_keys();
 void launch_attn_decode(int dtype, const void* q, const void* kc,
                         const void* vc, const int32_t* pos, int B, int H,
-                        int hs, int Tb, float* part, int32_t* counters,
-                        void* y, hipStream_t s);
+                        int hs, int Tb, float* part, void* y,
+                        bool merge_into_y, hipStream_t s);
+
+// Decode output projection fed directly by the attention records:
+// x[m] += merge(part[m]) W^T + b for M <= 4 rows (see decode_fused_proj).
+bool decode_fused_proj(int M);
+void launch_attn_proj(int dtype, const float* part, const int32_t* pos, int H,
+                      int hs, int nchunk, int chunk_keys, const void* W, int M,
+                      int C, const EpiArgs& e, hipStream_t s);
 
 // Argument pack of the sampler kernel, used to (re)write its graph node.
 struct SamplerArgs {
@@ -99,15 +123,19 @@ struct SamplerArgs {
   int32_t* lens = nullptr;
   const int32_t* limit = nullptr;
   int32_t* status = nullptr;
-  void* ptrs[13] = {};
+  // decode steps also write the embedding x = wte[id] + wpe[pos] (fp32 [B][C])
+  const void* wte = nullptr;
+  const void* wpe = nullptr;
+  int C = 0;
+  int dtype = 0;
+  float* x = nullptr;
+  void* ptrs[18] = {};
 };
 // Fill a kernel-node description for B rows; `a` must outlive its use.
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
 
-void launch_sampler(int mode, const float* logits, int ld, int B, int V,
-                    const double* uniforms, const SampleParams* params,
-                    const int32_t* feed_ids, int32_t* next_ids, int32_t* tok,
-                    int32_t* pos, int32_t* lens, const int32_t* limit,
-                    int32_t* status, hipStream_t s);
+// Sampler / feed head node: picks each row's next id and, in the step modes,
+// sets tok/pos, advances lens and writes the row's embedding.
+void launch_sampler(const SamplerArgs& a, int B, hipStream_t s);
 
 }  // namespace ngpt

@@ -65,7 +65,8 @@ extern "C" {
  * Model shape, the GPTConfig of the SDK guide ("模型架构解析"): block_size,
  * vocab_size, n_layer, n_head, n_embd, bias.  dropout is absent (inference).
  * Supported: n_embd % n_head == 0; head_dim = n_embd / n_head in {32, 64};
- * n_embd % 64 == 0 (bf16) or n_embd % 4 == 0 (fp32); 1 <= block_size <= 4096;
+ * n_embd % 64 == 0 (bf16) or n_embd % 4 == 0 (fp32); n_embd <= 2048;
+ * 1 <= block_size <= 4096;
  * vocab_size >= 1; max_batch in [1, NGPT_MAX_BATCH];
  * max_prefill_tokens >= 1 bounds the sum of prompt lengths of one prefill.
  */
