@@ -73,3 +73,32 @@ class Timer:
 
     def __exit__(self, *exc):
         log(f"{self.what}: {time.time() - self.t:.2f}s")
+
+
+def draws_must_agree(ref_logits, got_logits, margins, temperature, top_k):
+    """Which draws are decided beyond doubt by both sides' logits.
+
+    With logit errors at most d per row, each scaled logit moves by at most
+    delta = d/T and each weight exp(s_i - m) by a factor within
+    exp(+-delta) (the common max cancels in the ratios).  A normalised
+    running sum F = c_i/S then moves by at most
+    F(1-F)(exp(2 delta) - 1) <= (exp(2 delta) - 1)/4.  A draw whose oracle
+    margin exceeds twice that bound must agree.  With a top-k filter the
+    k-th and (k+1)-th scaled logits must also be more than 2 delta apart, so
+    that both sides keep the same set.
+    """
+    ref = np.asarray(ref_logits, np.float64)
+    got = np.asarray(got_logits, np.float64)
+    delta = np.max(np.abs(ref - got), axis=1) / temperature
+    need = margins > 0.5 * (np.exp(2.0 * delta) - 1.0)
+    if top_k and top_k < ref.shape[1]:
+        s = np.sort(ref / temperature, axis=1)[:, ::-1]
+        gap = s[:, top_k - 1] - s[:, top_k]
+        need &= gap > 2.0 * delta
+    return need
+
+
+def greedy_must_agree(ref_logits, tol):
+    """Rows whose oracle top-1 / top-2 gap exceeds twice the tolerance."""
+    s = np.sort(np.asarray(ref_logits, np.float64), axis=1)
+    return (s[:, -1] - s[:, -2]) > 2.0 * tol

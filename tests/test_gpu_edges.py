@@ -1,0 +1,214 @@
+"""GPU edge cases: degenerate lengths, limits, error paths forced from the
+host, batch-size boundaries between kernel families, determinism, KV-cached
+decode against a full recompute on the GPU, graph argument updates."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import (TOL_BF16, TOL_F32, dev_f64, dev_i32, gpu_prefill, log,
+                        make_model, make_oracle, max_abs, need_gpu, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def small(dtype="bf16", L=2, H=4, C=256, Tb=96, V=300, bias=True, batch=4):
+    return synth.Workload(f"edge_{dtype}_{C}_{H}", 11, L, H, C, Tb, V, V, bias,
+                          dtype, batch=batch, prompt_len=8)
+
+
+@pytest.mark.parametrize("dtype,H,C", [("bf16", 4, 256), ("bf16", 4, 128),
+                                       ("f32", 4, 128), ("f32", 2, 128)])
+def test_ragged_prefill_decode_head_sizes(dtype, H, C):
+    """hs = 64 and 32, bf16 and fp32, biases and non-unit LayerNorm weights,
+    ragged lengths including a single-token prompt."""
+    need_gpu()
+    w = small(dtype, H=H, C=C)
+    W = synth.make_weights(w, gamma_std=0.1)
+    rng = np.random.default_rng(5)
+    lens = np.array([1, 17, 64, 33], np.int32)
+    ids = rng.integers(0, w.vocab_size, (4, 64)).astype(np.int32)
+    o = make_oracle(w, W)
+    ref = [o.prefill(ids, lens)]
+    m = make_model(w, W)
+    kv = m.new_kv(4)
+    got = [gpu_prefill(m, kv, ids, lens)]
+    for s in range(6):
+        t = rng.integers(0, w.vocab_size, 4).astype(np.int32)
+        m.decode_feed(kv, dev_i32(t))
+        got.append(m.logits(4).cpu().numpy())
+        ref.append(o.decode(t))
+    errs = [max_abs(a, b) for a, b in zip(got, ref)]
+    log(f"  {dtype} hs={C // H}: max err {max(errs):.2e}")
+    assert max(errs) < tol_for(w)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 65])
+def test_batch_sizes_across_kernel_families(B):
+    """Decode batches on both sides of the streaming/MFMA boundary give the
+    oracle's logits and every row equals the same row run alone."""
+    need_gpu()
+    w = small("bf16", batch=B, L=1, Tb=64)
+    W = synth.make_weights(w)
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 30, B).astype(np.int32)
+    ids = rng.integers(0, w.vocab_size, (B, 30)).astype(np.int32)
+    o = make_oracle(w, W)
+    ref = o.prefill(ids, lens)
+    m = make_model(w, W, max_batch=max(B, 1))
+    kv = m.new_kv(B)
+    got = gpu_prefill(m, kv, ids, lens)
+    t = rng.integers(0, w.vocab_size, B).astype(np.int32)
+    m.decode_feed(kv, dev_i32(t))
+    got2 = m.logits(B).cpu().numpy()
+    ref2 = o.decode(t)
+    assert max_abs(got, ref) < TOL_BF16 and max_abs(got2, ref2) < TOL_BF16
+
+
+def test_zero_layer_model_closed_form():
+    """n_layer = 0: logits = ln_f(wte[id] + wpe[pos]) wte^T."""
+    need_gpu()
+    w = dataclasses.replace(small("f32", bias=True), n_layer=0)
+    W = synth.make_weights(w, gamma_std=0.1)
+    ids = np.array([[3, 7, 250, 1]], np.int32)
+    m = make_model(w, W, max_batch=1)
+    kv = m.new_kv(1)
+    got = gpu_prefill(m, kv, ids, [4])
+    x = W["wte"][250].astype(np.float64) + W["wpe"][2]
+    ids2 = np.array([[3, 7, 250]], np.int32)
+    got3 = gpu_prefill(m, kv, ids2, [3])
+    z = oracle.layer_norm(x, W["lnf_w"], W["lnf_b"])
+    assert max_abs(got3[0], W["wte"].astype(np.float64) @ z) < TOL_F32
+    assert max_abs(got[0], make_oracle(w, W).prefill(ids, [4])[0]) < TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kv_decode_matches_gpu_full_recompute(dtype):
+    """Logits after prefill(p) + k fed steps equal a prefill of the whole
+    p+k sequence (within the path's tolerance)."""
+    need_gpu()
+    w = small(dtype, batch=2)
+    W = synth.make_weights(w)
+    rng = np.random.default_rng(9)
+    seq = rng.integers(0, w.vocab_size, (2, 40)).astype(np.int32)
+    m = make_model(w, W)
+    kv = m.new_kv(2)
+    gpu_prefill(m, kv, seq[:, :25], [25, 25])
+    for s in range(25, 40):
+        m.decode_feed(kv, dev_i32(seq[:, s]))
+    dec = m.logits(2).cpu().numpy()
+    kv2 = m.new_kv(2)
+    full = gpu_prefill(m, kv2, seq, [40, 40])
+    log(f"  {dtype}: decode vs recompute {max_abs(dec, full):.2e}")
+    assert max_abs(dec, full) < tol_for(w)
+
+
+def test_limits_inactive_rows_and_context_error():
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    w = small("bf16", batch=3, Tb=32)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(3).integers(0, w.vocab_size, (3, 32)).astype(np.int32)
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(3)
+    m.prefill(kv, dev_i32(ids), [30, 5, 32], [31, 7, 32])
+    before = m.logits(3).cpu().numpy()
+    nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+    m.decode_step(kv, nxt, None)
+    ids1 = nxt.cpu().numpy()
+    assert ids1[2] == -1 and ids1[0] >= 0 and ids1[1] >= 0
+    after = m.logits(3).cpu().numpy()
+    np.testing.assert_array_equal(after[2], before[2])   # untouched row
+    m.decode_step(kv, nxt, None)
+    ids2 = nxt.cpu().numpy()
+    assert ids2[0] == -1 and ids2[1] >= 0 and ids2[2] == -1
+    assert kv.lens.cpu().tolist() == [31, 7, 32]
+    with pytest.raises(ng.NgptError) as ei:
+        m.decode_step(kv, nxt, None)
+    assert ei.value.code == ng.NGPT_E_CONTEXT
+    assert m.device_status() == 0
+
+
+def test_host_validation_errors():
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    w = small("bf16", batch=2, Tb=32)
+    W = synth.make_weights(w)
+    m = make_model(w, W, max_prefill_tokens=40)
+    kv = m.new_kv(2)
+    ids = dev_i32(np.zeros((2, 32)))
+    cases = [
+        (([0, 5], None), ng.NGPT_E_RANGE),       # empty prompt
+        (([33, 5], None), ng.NGPT_E_RANGE),      # longer than block_size
+        (([30, 20], None), ng.NGPT_E_SIZE),      # sum above max_prefill_tokens
+        (([5, 5], [4, 32]), ng.NGPT_E_RANGE),    # limit below length
+        (([5, 5], [5, 33]), ng.NGPT_E_RANGE),    # limit above block_size
+    ]
+    for (lens, limit), code in cases:
+        with pytest.raises(ng.NgptError) as ei:
+            m.prefill(kv, ids, lens, limit)
+        assert ei.value.code == code, (lens, limit)
+    with pytest.raises(ng.NgptError) as ei:      # B larger than the kv batch
+        m.prefill(kv, dev_i32(np.zeros((3, 4))), [4, 4, 4])
+    assert ei.value.code == ng.NGPT_E_ARG
+    m.set_sampling(temperature=1.0, top_k=0, greedy=False)
+    m.prefill(kv, ids, [4, 4])
+    with pytest.raises(ng.NgptError) as ei:      # sampling needs uniforms
+        m.decode_step(kv, torch.empty(2, dtype=torch.int32, device="cuda"), None)
+    assert ei.value.code == ng.NGPT_E_ARG
+    with pytest.raises(ng.NgptError):
+        m.set_sampling(temperature=0.0, top_k=0, greedy=False)
+
+
+def test_out_of_range_ids_are_reported_not_faulted():
+    need_gpu()
+    import gpt_decoder_amd as ng
+    w = small("bf16", batch=1)
+    m = make_model(w, synth.make_weights(w))
+    kv = m.new_kv(1)
+    m.prefill(kv, dev_i32([[1, 2, w.vocab_size + 5, 3]]), [4])
+    assert m.device_status() == ng.NGPT_E_DEVICE
+    assert m.device_status() == ng.NGPT_OK       # cleared
+    m.decode_feed(kv, dev_i32([-1]))
+    assert m.device_status() == ng.NGPT_E_DEVICE
+
+
+def test_bitwise_determinism_and_graph_argument_updates():
+    """Two identical runs give bitwise-identical logits and ids; changing the
+    next_ids / uniforms buffers between steps (graph node update) and the
+    sampling parameters (device-resident) behaves like fresh buffers."""
+    torch = need_gpu()
+    w = small("bf16", batch=4, Tb=64)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(2).integers(0, w.vocab_size, (4, 10)).astype(np.int32)
+    uni = np.random.default_rng(4).random((12, 4))
+
+    def run(switch_buffers):
+        m = make_model(w, W)
+        m.set_sampling(temperature=0.9, top_k=20)
+        kv = m.new_kv(4)
+        m.prefill(kv, dev_i32(ids), [10] * 4)
+        bufs = [torch.empty(4, dtype=torch.int32, device="cuda") for _ in range(2)]
+        ubufs = [dev_f64(uni[s]) for s in range(12)]
+        out, lg = [], []
+        for s in range(12):
+            if s == 6:
+                m.set_sampling(greedy=True)
+            nb = bufs[s % 2] if switch_buffers else bufs[0]
+            m.decode_step(kv, nb, ubufs[s])
+            out.append(nb.cpu().numpy().copy())
+            lg.append(m.logits(4).cpu().numpy())
+        m.close()
+        return np.array(out), np.array(lg)
+
+    a_ids, a_lg = run(False)
+    b_ids, b_lg = run(True)
+    np.testing.assert_array_equal(a_ids, b_ids)
+    np.testing.assert_array_equal(a_lg, b_lg)
+    # from step 6 on the draws are greedy: each id is the argmax of the
+    # previous step's logits
+    for s in range(6, 12):
+        np.testing.assert_array_equal(a_ids[s], np.argmax(a_lg[s - 1], axis=1))
