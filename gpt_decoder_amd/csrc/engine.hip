@@ -97,6 +97,13 @@ struct ngpt_model {
   int32_t *tok = nullptr, *pos = nullptr, *status = nullptr;
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
+  // one-launch batch-1 decode (see k_persist.hip)
+  int grid_cus = 0;
+  bool persist = false;
+  PersistLayer* d_layers = nullptr;
+  uint64_t *e_qkv = nullptr, *e_rec = nullptr, *e_y = nullptr, *e_x1 = nullptr,
+           *e_f = nullptr, *e_x2 = nullptr;
+  uint32_t* epoch = nullptr;
   // host record of the KV batch state
   std::vector<int32_t> h_lens, h_limit;
   GraphSlot g_step, g_feed;
@@ -210,6 +217,24 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
                o_tok = carve(Bm * 4),
                o_pos = carve(Bm * 4), o_st = carve(16),
                o_prm = carve(sizeof(SampleParams));
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess) cus = 0;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  }
+  m->grid_cus = cus;
+  m->persist = persistent_decode_supported(cfg->dtype, m->C, m->H, m->L, m->Tb, 1, cus);
+  const size_t L = m->L, SL = (size_t)persistent_exchange_slack();
+  const size_t o_eq = m->persist ? carve((L * 3 * C + SL) * 8) : 0,
+               o_er = m->persist ? carve((L * m->H * (size_t)m->nchunk * (m->hs + 2) + SL) * 8) : 0,
+               o_ey = m->persist ? carve((L * C + SL) * 8) : 0,
+               o_e1 = m->persist ? carve((L * C + SL) * 8) : 0,
+               o_ef = m->persist ? carve((L * 4 * C + SL) * 8) : 0,
+               o_e2 = m->persist ? carve((L * C + SL) * 8) : 0,
+               o_ep = m->persist ? carve(16) : 0,
+               o_dl = m->persist ? carve(L * sizeof(PersistLayer)) : 0;
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
     delete m;
@@ -224,11 +249,29 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
   m->tok = (int32_t*)(base + o_tok);
   m->pos = (int32_t*)(base + o_pos); m->status = (int32_t*)(base + o_st);
   m->params = (SampleParams*)(base + o_prm);
+  std::vector<PersistLayer> hl;
+  if (m->persist) {
+    m->e_qkv = (uint64_t*)(base + o_eq); m->e_rec = (uint64_t*)(base + o_er);
+    m->e_y = (uint64_t*)(base + o_ey); m->e_x1 = (uint64_t*)(base + o_e1);
+    m->e_f = (uint64_t*)(base + o_ef); m->e_x2 = (uint64_t*)(base + o_e2);
+    m->epoch = (uint32_t*)(base + o_ep);
+    m->d_layers = (PersistLayer*)(base + o_dl);
+    for (const ngpt_layer_weights& lw : m->layers)
+      hl.push_back(PersistLayer{(const bf16_t*)lw.ln1_w, (const bf16_t*)lw.ln1_b,
+                                (const bf16_t*)lw.attn_w, (const bf16_t*)lw.attn_b,
+                                (const bf16_t*)lw.attnproj_w, (const bf16_t*)lw.attnproj_b,
+                                (const bf16_t*)lw.ln2_w, (const bf16_t*)lw.ln2_b,
+                                (const bf16_t*)lw.fc_w, (const bf16_t*)lw.fc_b,
+                                (const bf16_t*)lw.mlpproj_w, (const bf16_t*)lw.mlpproj_b});
+  }
   e = hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipMemsetAsync(m->ws, 0, off, m->stream);
   SampleParams p{1.0f, 0, 1, 0};
   if (e == hipSuccess)
     e = hipMemcpyAsync(m->params, &p, sizeof(p), hipMemcpyHostToDevice, m->stream);
+  if (e == hipSuccess && m->persist)
+    e = hipMemcpyAsync(m->d_layers, hl.data(), hl.size() * sizeof(PersistLayer),
+                       hipMemcpyHostToDevice, m->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
   if (e != hipSuccess) {
     std::string msg = std::string("workspace init: ") + hipGetErrorString(e);
@@ -366,6 +409,25 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
 // embedding x = wte[tok] + wpe[pos] of every row.
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
+  if (m->persist && Bk == 1) {
+    PersistArgs a{};
+    a.L = m->L; a.H = m->H; a.C = C; a.V = m->V; a.Tb = m->Tb;
+    a.nchunk = m->nchunk;
+    a.sv_floats = persistent_sv_floats(C, m->nchunk);
+    a.wte = (const bf16_t*)m->wte; a.wpe = (const bf16_t*)m->wpe;
+    a.lnf_w = (const bf16_t*)m->lnf_w; a.lnf_b = (const bf16_t*)m->lnf_b;
+    a.layers = m->d_layers;
+    a.pos = m->pos;
+    a.x0 = m->x;
+    a.kc = (bf16_t*)kv->k; a.vc = (bf16_t*)kv->v;
+    a.layer_stride = (size_t)m->H * m->Tb * m->hs;
+    a.logits = m->logits;
+    a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
+    a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
+    a.epoch = m->epoch; a.status = m->status;
+    launch_decode_persistent(a, m->grid_cus, s);
+    return;
+  }
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, Bk);

@@ -7,6 +7,10 @@
 #include "ngpt.h"
 
 namespace ngpt {
+typedef uint16_t bf16_t;
+}
+
+namespace ngpt {
 
 // Packed prefill rows: sequence b owns rows [off[b], off[b+1]).
 struct RowMap {
@@ -137,5 +141,36 @@ void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
 // Sampler / feed head node: picks each row's next id and, in the step modes,
 // sets tok/pos, advances lens and writes the row's embedding.
 void launch_sampler(const SamplerArgs& a, int B, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// One-launch decode step for batch 1 (bf16, head size 64, n_embd <= 1024).
+struct PersistLayer {
+  const bf16_t *ln1_w, *ln1_b, *attn_w, *attn_b, *proj_w, *proj_b;
+  const bf16_t *ln2_w, *ln2_b, *fc_w, *fc_b, *mp_w, *mp_b;
+};
+
+struct PersistArgs {
+  int L, H, C, V, Tb, nchunk, sv_floats;
+  const bf16_t *wte, *wpe, *lnf_w, *lnf_b;
+  const PersistLayer* layers;   // device array [L]
+  const int32_t* pos;           // [1], set by the head node (< 0: inactive)
+  const float* x0;              // [C] embedding written by the head node
+  bf16_t* kc;                   // cache bases and per-layer stride (elements)
+  bf16_t* vc;
+  size_t layer_stride;
+  float* logits;                // [V]
+  // exchange words (fp32 value | epoch << 32), per layer
+  uint64_t *e_qkv, *e_rec, *e_y, *e_x1, *e_f, *e_x2;
+  uint32_t* epoch;              // advanced once per launch
+  int32_t* status;              // bit 1: a wait timed out
+};
+
+bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,
+                                 int batch, int grid);
+size_t persistent_lds_bytes(int C, int nchunk);
+int persistent_sv_floats(int C, int nchunk);
+// words of slack past the end of each exchange buffer (polls read ahead)
+int persistent_exchange_slack();
+void launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t s);
 
 }  // namespace ngpt
