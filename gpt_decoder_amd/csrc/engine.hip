@@ -413,7 +413,6 @@ static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t
     PersistArgs a{};
     a.L = m->L; a.H = m->H; a.C = C; a.V = m->V; a.Tb = m->Tb;
     a.nchunk = m->nchunk;
-    a.sv_floats = persistent_sv_floats(C, m->nchunk);
     a.wte = (const bf16_t*)m->wte; a.wpe = (const bf16_t*)m->wpe;
     a.lnf_w = (const bf16_t*)m->lnf_w; a.lnf_b = (const bf16_t*)m->lnf_b;
     a.layers = m->d_layers;

@@ -150,7 +150,7 @@ struct PersistLayer {
 };
 
 struct PersistArgs {
-  int L, H, C, V, Tb, nchunk, sv_floats;
+  int L, H, C, V, Tb, nchunk;
   const bf16_t *wte, *wpe, *lnf_w, *lnf_b;
   const PersistLayer* layers;   // device array [L]
   const int32_t* pos;           // [1], set by the head node (< 0: inactive)
@@ -167,8 +167,7 @@ struct PersistArgs {
 
 bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,
                                  int batch, int grid);
-size_t persistent_lds_bytes(int C, int nchunk);
-int persistent_sv_floats(int C, int nchunk);
+size_t persistent_lds_bytes(int C, int L);
 // words of slack past the end of each exchange buffer (polls read ahead)
 int persistent_exchange_slack();
 void launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t s);
