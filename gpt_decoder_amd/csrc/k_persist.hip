@@ -49,8 +49,9 @@ namespace ngpt {
 namespace {
 
 constexpr int kCompute = 4;                 // compute wavefronts
-constexpr int kThreads = 64 * (kCompute + 1);
-constexpr int kSyncWave = kCompute;
+constexpr int kNSync = 2;                   // sync wavefronts (after the compute ones)
+constexpr int kThreads = 64 * (kCompute + kNSync);
+constexpr int kSyncLanes = 64 * kNSync;
 constexpr int kSpinLimit = 1 << 20;
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr int kHs = 64;          // head size
@@ -148,10 +149,11 @@ __device__ __forceinline__ void put_word(float* dst, int k, uint64_t v) {
     dst[k] = __uint_as_float(x);
 }
 
-// Called by the whole sync wavefront: wait until src[0..n) all carry epoch
-// ep and copy the values to dst (LDS).  n <= 64 * NJ; the words up to
-// src[64 * NJ) are read too (the exchange buffers carry that much slack) and
-// ignored.  Every pass issues all NJ loads before inspecting any, and copies
+// Called by every sync wavefront: wait until src[0..n) all carry epoch ep
+// and copy the values to dst (LDS).  Sync lane s (of kSyncLanes) polls words
+// s + kSyncLanes * j, j < NJ; n <= kSyncLanes * NJ, and the words up to
+// src[kSyncLanes * NJ) are read too (the exchange buffers carry that much
+// slack) and ignored.  Every pass issues all NJ loads before inspecting any, and copies
 // every word that carries ep (a word does not change once tagged, so copying
 // it again is harmless); the wait ends on the first pass with nothing
 // missing.  No per-word bookkeeping is carried between passes.  False after
@@ -160,22 +162,22 @@ template <int NJ, bool PACK>
 __device__ __forceinline__ bool sync_wave_wait(const uint64_t* src, int n,
                                                uint32_t ep, float* dst,
                                                int32_t* status) {
-  const int lane = threadIdx.x & 63;
+  const int sl = static_cast<int>(threadIdx.x) - 64 * kCompute;
   for (int spin = 0;; ++spin) {
     uint64_t v[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) v[j] = tag_load(src + lane + 64 * j);
+    for (int j = 0; j < NJ; ++j) v[j] = tag_load(src + sl + kSyncLanes * j);
     bool miss = false;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const bool in = lane + 64 * j < n;
+      const bool in = sl + kSyncLanes * j < n;
       const bool got = static_cast<uint32_t>(v[j] >> 32) == ep;
-      if (in && got) put_word<PACK>(dst, lane + 64 * j, v[j]);
+      if (in && got) put_word<PACK>(dst, sl + kSyncLanes * j, v[j]);
       miss |= in && !got;
     }
     if (!__any(miss)) return true;
     if (spin >= kSpinLimit) {
-      if (lane == 0) atomicOr(status, 2);
+      if ((sl & 63) == 0) atomicOr(status, 2);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -210,34 +212,35 @@ __device__ __forceinline__ bool sync_wave_wait_qkv(const uint64_t* e, int qo, in
 }
 
 // The waits of one launch, by the number of words they read; each picks the
-// smallest load count that covers n.  Reads past n stay below 512 words, the
-// exchange buffers' slack.
+// smallest load count that covers n (in rounds of kSyncLanes words).  Reads
+// past n stay below 512 words, the exchange buffers' slack.
 //   kWaitRec   attention records of one head: n <= 512 fp32 words
 //   kWaitY     y: C/2 packed words (32..384)
 //   kWaitC     x1 or x2: C fp32 words (64..768)
 //   kWaitF     f: 2C packed words (128..1536)
 enum WaitKind { kWaitRec, kWaitY, kWaitC, kWaitF };
+static_assert(kSyncLanes == 128, "the load counts below assume two sync wavefronts");
 
 template <int KIND>
 __device__ __forceinline__ bool sync_wave_wait_n(const uint64_t* src, int n,
                                                  uint32_t ep, float* dst,
                                                  int32_t* status) {
   if constexpr (KIND == kWaitRec) {
-    if (n <= 128) return sync_wave_wait<2, false>(src, n, ep, dst, status);
-    if (n <= 256) return sync_wave_wait<4, false>(src, n, ep, dst, status);
-    return sync_wave_wait<8, false>(src, n, ep, dst, status);
+    if (n <= 128) return sync_wave_wait<1, false>(src, n, ep, dst, status);
+    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, status);
+    return sync_wave_wait<4, false>(src, n, ep, dst, status);
   } else if constexpr (KIND == kWaitY) {
-    if (n <= 128) return sync_wave_wait<2, true>(src, n, ep, dst, status);
-    if (n <= 256) return sync_wave_wait<4, true>(src, n, ep, dst, status);
-    return sync_wave_wait<6, true>(src, n, ep, dst, status);
+    if (n <= 128) return sync_wave_wait<1, true>(src, n, ep, dst, status);
+    if (n <= 256) return sync_wave_wait<2, true>(src, n, ep, dst, status);
+    return sync_wave_wait<3, true>(src, n, ep, dst, status);
   } else if constexpr (KIND == kWaitC) {
-    if (n <= 256) return sync_wave_wait<4, false>(src, n, ep, dst, status);
-    if (n <= 512) return sync_wave_wait<8, false>(src, n, ep, dst, status);
-    return sync_wave_wait<12, false>(src, n, ep, dst, status);
+    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, status);
+    if (n <= 512) return sync_wave_wait<4, false>(src, n, ep, dst, status);
+    return sync_wave_wait<6, false>(src, n, ep, dst, status);
   } else {
-    if (n <= 512) return sync_wave_wait<8, true>(src, n, ep, dst, status);
-    if (n <= 1024) return sync_wave_wait<16, true>(src, n, ep, dst, status);
-    return sync_wave_wait<24, true>(src, n, ep, dst, status);
+    if (n <= 512) return sync_wave_wait<4, true>(src, n, ep, dst, status);
+    if (n <= 1024) return sync_wave_wait<8, true>(src, n, ep, dst, status);
+    return sync_wave_wait<12, true>(src, n, ep, dst, status);
   }
 }
 
@@ -493,6 +496,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
   bf16_t* sln = reinterpret_cast<bf16_t*>(sq + 3 * kHs);  // [2][4][C]
   uint64_t* slay = reinterpret_cast<uint64_t*>(sq + 3 * kHs + 4 * C);  // [L][12]
 
+  const bool sync0 = SYNC && __builtin_amdgcn_readfirstlane(wave) == kCompute;  // first sync wavefront
   int seq = 0;
   // n == 0: nothing to poll, the wait is just the barrier
   auto wait_in = [&](auto kind, const uint64_t* src, int n, float* dst) -> bool {
@@ -512,7 +516,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
   using WF = std::integral_constant<int, kWaitF>;
 
   LnStage lns;
-  if constexpr (SYNC) {
+  if (sync0) {
     const PersistLayer& q = a.layers[0];
     const bf16_t* rows[4] = {q.ln1_w, q.ln1_b, q.ln2_w, q.ln2_b};
     lns.load(rows, 4, C);
@@ -522,7 +526,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
     const uint64_t* src = reinterpret_cast<const uint64_t*>(a.layers);
     for (int i = tid; i < L * kLayerPtrs; i += kThreads) slay[i] = src[i];
   }
-  if constexpr (SYNC) lns.store(sln, C);
+  if (sync0) lns.store(sln, C);
   __syncthreads();
   // weight pointers of block l as scalars (the table in global memory could
   // only be read with vector loads, which would queue behind the prefetches)
@@ -614,7 +618,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
       const int h = h0, it = it0;
       const bool last = (it == nitem - 1);  // holds the new key p
       ++seq;   // wait: q of head h (with the new k, v for the last item)
-      if constexpr (SYNC) {
+      if (sync0) {
         if (!sync_wave_wait_qkv(e_qkv, h * kHs / 2, (C + h * kHs) / 2, (2 * C + h * kHs) / 2,
                                 last, ep, sq, a.status) && lane == 0)
           S.fail = seq;
@@ -730,9 +734,9 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
     // ---- C: c_proj rows + residual ------------------------------------
     // (the sync wavefront stages the next block's LayerNorm rows, or ln_f,
     // into the other parity's LDS rows, last read two blocks back)
-    if constexpr (SYNC) stage(l + 1);
+    if (sync0) stage(l + 1);
     ok = wait_in(WY{}, e_y, C / 2, bY);
-    if constexpr (SYNC) lns.store(sln + (size_t)((l + 1) & 1) * 4 * C, C);
+    if (sync0) lns.store(sln + (size_t)((l + 1) & 1) * 4 * C, C);
     if (!ok) break;
     if constexpr (!SYNC) {
       const bf16_t* bias = lptr(l, kProjB);
@@ -819,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
   // run, breaking the pairing of the roles' barriers.
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   if (p >= 0) {
-    if (wv == kSyncWave)
+    if (wv >= kCompute)
       run_role<true>(a, smem, S, ep, p);
     else
       run_role<false>(a, smem, S, ep, p);
