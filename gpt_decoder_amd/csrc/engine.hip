@@ -104,6 +104,8 @@ struct ngpt_model {
   uint64_t *e_qkv = nullptr, *e_rec = nullptr, *e_y = nullptr, *e_x1 = nullptr,
            *e_f = nullptr, *e_x2 = nullptr;
   uint32_t* epoch = nullptr;
+  uint64_t* e_cand = nullptr;   // greedy candidates left by the last launch
+  bool cand_ok = false;         // the current logits came from that launch
   // host record of the KV batch state
   std::vector<int32_t> h_lens, h_limit;
   GraphSlot g_step, g_feed;
@@ -234,6 +236,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
                o_ef = m->persist ? carve((L * 4 * C + SL) * 8) : 0,
                o_e2 = m->persist ? carve((L * C + SL) * 8) : 0,
                o_ep = m->persist ? carve(16) : 0,
+               o_ec = m->persist ? carve((2 * (size_t)cus + SL) * 8) : 0,
                o_dl = m->persist ? carve(L * sizeof(PersistLayer)) : 0;
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
@@ -255,6 +258,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
     m->e_y = (uint64_t*)(base + o_ey); m->e_x1 = (uint64_t*)(base + o_e1);
     m->e_f = (uint64_t*)(base + o_ef); m->e_x2 = (uint64_t*)(base + o_e2);
     m->epoch = (uint32_t*)(base + o_ep);
+    m->e_cand = (uint64_t*)(base + o_ec);
     m->d_layers = (PersistLayer*)(base + o_dl);
     for (const ngpt_layer_weights& lw : m->layers)
       hl.push_back(PersistLayer{(const bf16_t*)lw.ln1_w, (const bf16_t*)lw.ln1_b,
@@ -364,6 +368,7 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
 
   const int M = (int)total, C = m->C, dt = m->cfg.dtype;
   hipStream_t s = m->stream;
+  m->cand_ok = false;   // the logits are about to come from this prefill
   set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(la, kv->lens, kv->limit);
   launch_embed_prefill(dt, ids, Tmax, map, M, m->wte, m->wpe, C, m->V, m->x,
                        m->row_b, m->row_pos, m->last_rows, m->status, s);
@@ -407,24 +412,31 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
 // The one-token forward shared by the step and feed graphs.  The head node
 // (sampler or feed) has already set tok/pos, advanced lens and written the
 // embedding x = wte[tok] + wpe[pos] of every row.
+static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
+  PersistArgs a{};
+  a.L = m->L; a.H = m->H; a.C = m->C; a.V = m->V; a.Tb = m->Tb;
+  a.nchunk = m->nchunk;
+  a.wte = (const bf16_t*)m->wte; a.wpe = (const bf16_t*)m->wpe;
+  a.lnf_w = (const bf16_t*)m->lnf_w; a.lnf_b = (const bf16_t*)m->lnf_b;
+  a.layers = m->d_layers;
+  a.pos = m->pos;
+  a.fused = 0;
+  a.lens = kv->lens; a.tok = m->tok; a.next_ids = nullptr;
+  a.e_cand = m->e_cand;
+  a.x0 = m->x;
+  a.kc = (bf16_t*)kv->k; a.vc = (bf16_t*)kv->v;
+  a.layer_stride = (size_t)m->H * m->Tb * m->hs;
+  a.logits = m->logits;
+  a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
+  a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
+  a.epoch = m->epoch; a.status = m->status;
+  return a;
+}
+
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
   if (m->persist && Bk == 1) {
-    PersistArgs a{};
-    a.L = m->L; a.H = m->H; a.C = C; a.V = m->V; a.Tb = m->Tb;
-    a.nchunk = m->nchunk;
-    a.wte = (const bf16_t*)m->wte; a.wpe = (const bf16_t*)m->wpe;
-    a.lnf_w = (const bf16_t*)m->lnf_w; a.lnf_b = (const bf16_t*)m->lnf_b;
-    a.layers = m->d_layers;
-    a.pos = m->pos;
-    a.x0 = m->x;
-    a.kc = (bf16_t*)kv->k; a.vc = (bf16_t*)kv->v;
-    a.layer_stride = (size_t)m->H * m->Tb * m->hs;
-    a.logits = m->logits;
-    a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
-    a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
-    a.epoch = m->epoch; a.status = m->status;
-    launch_decode_persistent(a, m->grid_cus, s);
+    launch_decode_persistent(persist_args(m, kv), m->grid_cus, s);
     return;
   }
   for (int l = 0; l < m->L; ++l) {
@@ -527,6 +539,18 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   bool any = false;
   for (int b = 0; b < kv->batch; ++b) any |= m->h_lens[b] < m->h_limit[b];
   if (!any) return fail(m, NGPT_E_CONTEXT, "no sequence can take another token");
+  // Greedy batch-1 step after a one-launch forward: the launch picks its own
+  // token from the candidates the previous one left, no head node.
+  if (mode == SAMPLE_STEP && m->h_params.greedy && m->persist && kv->batch == 1 &&
+      m->cand_ok) {
+    PersistArgs a = persist_args(m, kv);
+    a.fused = 1;
+    a.next_ids = arg_out;
+    launch_decode_persistent(a, m->grid_cus, m->stream);
+    HIP_TRY(m, hipGetLastError());
+    if (m->h_lens[0] < m->h_limit[0]) ++m->h_lens[0];
+    return NGPT_OK;
+  }
   const bool same_kv = g.exec && g.k == kv->k && g.v == kv->v &&
                        g.lens == kv->lens && g.limit == kv->limit &&
                        g.batch == kv->batch;
@@ -543,6 +567,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
     g.arg_out = arg_out;
   }
   HIP_TRY(m, hipGraphLaunch(g.exec, m->stream));
+  m->cand_ok = m->persist && kv->batch == 1;
   for (int b = 0; b < kv->batch; ++b)
     if (m->h_lens[b] < m->h_limit[b]) ++m->h_lens[b];
   return NGPT_OK;

@@ -462,17 +462,37 @@ __device__ __forceinline__ int split_lo(int n, int parts, int i) {
 }
 
 // LDS layout (floats): x, x1, y [C] each, f [4C], records [kRecWords],
-// q/k/v [3][64], the LayerNorm rows [2 parities][4][C] bf16, then the
-// blocks' weight pointers [L][12] (uint64).
+// q/k/v [3][64], the LayerNorm rows [2 parities][4][C] bf16, the greedy
+// candidates of the previous launch [G][2], then the blocks' weight
+// pointers [L][12] (uint64).
 constexpr int kLayerPtrs = sizeof(PersistLayer) / sizeof(uint64_t);
+constexpr int kMaxGrid = 256;   // candidates: 2 words per workgroup, <= 512 words
 __host__ __device__ constexpr int lds_floats(int C, int L) {
-  return 11 * C + kRecWords + 3 * kHs + 2 * kLayerPtrs * L;
+  return 11 * C + kRecWords + 3 * kHs + 2 * kMaxGrid + 2 * kLayerPtrs * L;
+}
+
+// Greedy choice, the sampler's rule: the largest logit, lowest id among
+// equal maxima; NaN and -inf never win (an all -inf/NaN row gives INT_MAX).
+__device__ __forceinline__ void cand_take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && v > -INFINITY && i < bi)) { bv = v; bi = i; }
+}
+// the best candidate over the wavefront, in every lane
+__device__ __forceinline__ void cand_wave(float& bv, int& bi) {
+  auto step = [&](float pv, float pib) { cand_take(bv, bi, pv, __float_as_int(pib)); };
+  step(lane_xor1(bv), lane_xor1(__int_as_float(bi)));
+  step(lane_xor2(bv), lane_xor2(__int_as_float(bi)));
+  step(lane_mirror8(bv), lane_mirror8(__int_as_float(bi)));
+  step(lane_xor8(bv), lane_xor8(__int_as_float(bi)));
+  step(lane_xor16(bv), lane_xor16(__int_as_float(bi)));
+  step(lane_xor32(bv), lane_xor32(__int_as_float(bi)));
 }
 
 }  // namespace
 
 struct PShared {
   float part[kCompute][kRec];
+  float cv[kCompute];   // greedy candidates of the compute wavefronts
+  int ci[kCompute];
   int fail;   // sequence number of the first wait that timed out
 };
 
@@ -494,7 +514,8 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
   float* bRec = bF + 4 * C;            // other items' records
   float* sq = bRec + kRecWords;        // q, new k, new v of one head
   bf16_t* sln = reinterpret_cast<bf16_t*>(sq + 3 * kHs);  // [2][4][C]
-  uint64_t* slay = reinterpret_cast<uint64_t*>(sq + 3 * kHs + 4 * C);  // [L][12]
+  float* bCand = sq + 3 * kHs + 4 * C;                  // [G][2]
+  uint64_t* slay = reinterpret_cast<uint64_t*>(bCand + 2 * kMaxGrid);  // [L][12]
 
   const bool sync0 = SYNC && __builtin_amdgcn_readfirstlane(wave) == kCompute;  // first sync wavefront
   int seq = 0;
@@ -521,7 +542,8 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
     const bf16_t* rows[4] = {q.ln1_w, q.ln1_b, q.ln2_w, q.ln2_b};
     lns.load(rows, 4, C);
   }
-  for (int i = tid; i < C; i += kThreads) bX[i] = a.x0[i];
+  if (!a.fused)
+    for (int i = tid; i < C; i += kThreads) bX[i] = a.x0[i];
   {
     const uint64_t* src = reinterpret_cast<const uint64_t*>(a.layers);
     for (int i = tid; i < L * kLayerPtrs; i += kThreads) slay[i] = src[i];
@@ -576,6 +598,43 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
   }
 
   bool ok = true;
+  if (a.fused) {
+    // Greedy step: the token is the argmax of the logits the previous launch
+    // produced, from its workgroups' candidates (tagged with its epoch);
+    // the sync wavefronts pick it and write x = wte[tok] + wpe[p].
+    ++seq;
+    if constexpr (SYNC) {
+      if (!sync_wave_wait<(2 * kMaxGrid) / kSyncLanes, false>(a.e_cand, 2 * G, ep - 1u, bCand,
+                                                                a.status) && lane == 0)
+        S.fail = seq;
+    }
+    __syncthreads();
+    ok = __builtin_amdgcn_readfirstlane(S.fail) > seq;
+    if (ok) {
+      if constexpr (SYNC) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int k = lane; k < G; k += 64) cand_take(bv, bi, bCand[2 * k], __float_as_int(bCand[2 * k + 1]));
+        cand_wave(bv, bi);
+        const int tok = bi;
+        const int sl = tid - 64 * kCompute;
+        if (tok >= 0 && tok < a.V) {
+          const bf16_t* te = a.wte + (size_t)tok * C;
+          const bf16_t* pe = a.wpe + (size_t)p * C;
+          for (int c = sl; c < C; c += kSyncLanes) bX[c] = to_f32(te[c]) + to_f32(pe[c]);
+        } else {
+          for (int c = sl; c < C; c += kSyncLanes) bX[c] = 0.f;
+          if (sl == 0) atomicOr(a.status, 1);
+        }
+        if (w == 0 && sl == 0) {
+          a.next_ids[0] = tok;
+          a.tok[0] = tok;
+          a.pos[0] = p;
+        }
+      }
+      __syncthreads();
+    }
+  }
   for (int l = 0; l < L && ok; ++l) {
     const bf16_t* lnr = sln + (size_t)(l & 1) * 4 * C;
     bf16_t* kl = a.kc + (size_t)l * a.layer_stride;
@@ -790,6 +849,8 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
     ok = wait_in(WC{}, a.e_x2 + (size_t)(L - 1) * C, C, bX);
     if (ok) {
       if constexpr (!SYNC) {
+        float bv = -INFINITY;   // this lane's greedy candidate over its rows
+        int bi = INT_MAX;
         const bf16_t* lnr = sln + (size_t)(L & 1) * 4 * C;
         float hv[2][8];
         wave_layernorm<2>(bX, C, lnr, lnr + C, hv);
@@ -799,12 +860,14 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
           grp(g + 1, g0, g1);
           nxt.load(a.wte, a.V, C, g0, g1);
           grp(g, g0, g1);
-          cur.dots_reg(hv, C, g0, g1, [&](int r, float v) { a.logits[r] = v; });
+          cur.dots_reg(hv, C, g0, g1, [&](int r, float v) { a.logits[r] = v; cand_take(bv, bi, v, r); });
           grp(g + 2, g0, g1);
           cur.load(a.wte, a.V, C, g0, g1);
           grp(g + 1, g0, g1);
-          nxt.dots_reg(hv, C, g0, g1, [&](int r, float v) { a.logits[r] = v; });
+          nxt.dots_reg(hv, C, g0, g1, [&](int r, float v) { a.logits[r] = v; cand_take(bv, bi, v, r); });
         }
+        cand_wave(bv, bi);
+        if (lane == 0) { S.cv[wave] = bv; S.ci[wave] = bi; }
       }
     }
   }
@@ -814,8 +877,11 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ PShared S;
   const uint32_t ep = *a.epoch + 1u;
-  const int p = a.pos[0];
+  // position of the new token: the sampler head node has set pos, or, in a
+  // fused greedy step, the current length (advanced at the end)
+  const int p = a.fused ? a.lens[0] : a.pos[0];
   if (threadIdx.x == 0) S.fail = INT_MAX;
+  if (threadIdx.x < kCompute) { S.cv[threadIdx.x] = -INFINITY; S.ci[threadIdx.x] = INT_MAX; }
   __syncthreads();
   // The role test must compile to a scalar branch: as a per-lane (divergent)
   // branch both roles' code would be laid out for every wavefront under exec
@@ -831,13 +897,24 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
   // the epoch advances once per launch; workgroup 0 finishes last among
   // the readers of the old value (its final phase waits for every block)
   __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.epoch = ep;
+  // this workgroup's greedy candidate for the next launch
+  if (threadIdx.x == 0 && p >= 0) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int i = 0; i < kCompute; ++i) cand_take(bv, bi, S.cv[i], S.ci[i]);
+    tag_store(a.e_cand + 2 * blockIdx.x, bv, ep);
+    tag_store(a.e_cand + 2 * blockIdx.x + 1, __int_as_float(bi), ep);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (a.fused && S.fail == INT_MAX) a.lens[0] = p + 1;
+    *a.epoch = ep;
+  }
 }
 
 bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,
                                  int batch, int grid) {
   if (dtype != NGPT_BF16 || batch != 1 || L < 1 || H * kHs != C) return false;
-  if (C > kMaxC || C % 64 != 0 || grid < 64) return false;
+  if (C > kMaxC || C % 64 != 0 || grid < 64 || grid > kMaxGrid) return false;
   // rows per workgroup must fit the register slabs: 4 per compute
   // wavefront for c_attn and c_fc (handed out in pairs), 1 for the two
   // projections

@@ -153,7 +153,13 @@ struct PersistArgs {
   int L, H, C, V, Tb, nchunk;
   const bf16_t *wte, *wpe, *lnf_w, *lnf_b;
   const PersistLayer* layers;   // device array [L]
-  const int32_t* pos;           // [1], set by the head node (< 0: inactive)
+  int32_t* pos;                 // [1]: set by the head node (< 0: inactive),
+                                // or written here in a fused greedy step
+  int fused;                    // 1: greedy step without a head node
+  int32_t* lens;                // kv lens [1] (fused: read, then advanced)
+  int32_t* tok;                 // fused: the chosen id ...
+  int32_t* next_ids;            // ... and the caller's copy
+  uint64_t* e_cand;             // greedy candidates, 2 words per workgroup
   const float* x0;              // [C] embedding written by the head node
   bf16_t* kc;                   // cache bases and per-layer stride (elements)
   bf16_t* vc;

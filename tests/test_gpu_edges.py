@@ -212,3 +212,70 @@ def test_bitwise_determinism_and_graph_argument_updates():
     # previous step's logits
     for s in range(6, 12):
         np.testing.assert_array_equal(a_ids[s], np.argmax(a_lg[s - 1], axis=1))
+
+
+def test_fused_greedy_step_matches_sampler_head_node():
+    """At batch 1 (bf16, head size 64) a greedy step that follows a one-launch
+    forward picks its id inside the launch, from the argmax candidates the
+    previous launch left behind; with top_k = 1 the same choice is made by
+    the sampler head node.  Ids, logits, lens and the whole KV cache must
+    agree bit for bit over a run that mixes a prefill, greedy steps, feed
+    steps, switched next_ids buffers and a second prefill (which makes the
+    candidates stale, so the next step must go through the head node)."""
+    torch = need_gpu()
+    w = small("bf16", L=3, H=4, C=256, Tb=160, V=300, bias=False, batch=1)
+    W = synth.make_weights(w, gamma_std=0.1)
+    # a larger (still bf16-exact) tied embedding makes the greedy ids move
+    # from step to step instead of settling on one token
+    W["wte"] = W["wte"] * np.float32(16.0)
+    rng = np.random.default_rng(17)
+    p1 = rng.integers(0, w.vocab_size, (1, 40)).astype(np.int32)
+    p2 = rng.integers(0, w.vocab_size, (1, 70)).astype(np.int32)
+    feed = rng.integers(0, w.vocab_size, (40,)).astype(np.int32)
+    uni = rng.random((40, 1))
+
+    def run(greedy):
+        m = make_model(w, W)
+        if greedy:
+            m.set_sampling(greedy=True)
+        else:
+            m.set_sampling(temperature=1.0, top_k=1)
+        kv = m.new_kv(1)
+        bufs = [torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+        ub = [dev_f64(uni[s]) for s in range(40)]
+        m.prefill(kv, dev_i32(p1), [40])
+        ids, lg = [], []
+        for s in range(40):
+            if s % 5 == 2:   # a fed id: the next step picks from new logits
+                m.decode_feed(kv, dev_i32(feed[s:s + 1]))
+            if s == 25:
+                m.prefill(kv, dev_i32(p2), [70])
+            nb = bufs[s % 2]
+            m.decode_step(kv, nb, ub[s])
+            ids.append(int(nb.cpu().numpy()[0]))
+            lg.append(m.logits(1).cpu().numpy()[0].copy())
+        out = (np.array(ids), np.array(lg), int(kv.lens.cpu().numpy()[0]),
+               kv.k.cpu().numpy().copy(), kv.v.cpu().numpy().copy())
+        assert m.device_status() == 0
+        m.close()
+        return out
+
+    g_ids, g_lg, g_len, g_k, g_v = run(True)
+    s_ids, s_lg, s_len, s_k, s_v = run(False)
+    log(f"  fused greedy ids {g_ids[:12]}..., final length {g_len}")
+    assert len(set(g_ids.tolist())) > 5, "ids too uniform to test the choice"
+    np.testing.assert_array_equal(g_ids, s_ids)
+    np.testing.assert_array_equal(g_lg, s_lg)
+    assert g_len == s_len == 70 + (40 - 25) + 3   # feeds at steps 27, 32, 37
+    # cache layout [L][B][H][Tb][64] bf16; positions past the length were
+    # never written (torch.empty)
+    shp = (w.n_layer, 1, w.n_head, w.block_size, w.n_embd // w.n_head)
+    for a_, b_ in ((g_k, s_k), (g_v, s_v)):
+        a_ = a_.view(np.uint16).reshape(shp)[:, :, :, :g_len]
+        b_ = b_.view(np.uint16).reshape(shp)[:, :, :, :g_len]
+        np.testing.assert_array_equal(a_, b_)
+    # each greedy id is the argmax of the logits before it (lowest id on ties)
+    for s in range(1, 40):
+        if s % 5 == 2 or s == 25:
+            continue
+        assert g_ids[s] == int(np.argmax(g_lg[s - 1]))
