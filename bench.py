@@ -25,6 +25,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
+DECODE_KERNEL = "decode_persistent_kernel"
+KERNEL_SOURCE = os.path.join(ROOT, "gpt_decoder_amd", "csrc", "k_persist.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_persistent_gpt2_124m_b1_traffic.txt")
 
 
 def decode_bytes_per_step(w, pos: int) -> int:
@@ -36,6 +39,36 @@ def decode_bytes_per_step(w, pos: int) -> int:
     ln = 2 * (2 * L + 1) * C
     kv = 2 * L * C * 2 * (pos + 1)
     return weights + ln + kv
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when that summary was taken on a different
+    version of the kernel source."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
+                      if ":" in line)
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != src:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(n_mib: int = 1024, reps: int = 5):
+    """A plain device copy of n_mib MiB (read n, write n), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    x = torch.ones(n_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n_mib * (1 << 20),
+                      "reps": reps}), flush=True)
 
 
 def prefill_flops(w, T: int) -> int:
@@ -73,11 +106,17 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--cpu-steps", type=int, default=192,
                     help="decode steps of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
               "supported (the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import gpt_decoder_amd as ng
@@ -99,12 +138,18 @@ def main():
     nxt = torch.empty(1, dtype=torch.int32, device="cuda")
     stream = m.stream
 
-    def generation(ev=None):
+    def generation(ev=None, kev=None):
         m.prefill(kv, d_ids, list(lens))
         if ev is not None:
             ev[0].record(stream)
-        for _ in range(n_new):
+        for s in range(n_new):
+            # after the first step each greedy step is one launch of the
+            # decode kernel on this stream: bracket those with events
+            if kev is not None and s > 0:
+                kev[s - 1][0].record(stream)
             m.decode_step(kv, nxt, None)
+            if kev is not None and s > 0:
+                kev[s - 1][1].record(stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -114,17 +159,25 @@ def main():
 
     evs = [(torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    kevs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_new - 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        generation(evs[k])
+        generation(evs[k], kevs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert m.device_status() == 0
     dec_ms = np.mean([a.elapsed_time(b) for a, b in evs])
     step_us = dec_ms * 1000.0 / n_new
-    avg_bytes = np.mean([decode_bytes_per_step(w, 128 + s) for s in range(n_new)])
-    dec_gbs = avg_bytes / (step_us * 1e-6) / 1e9
+    # dominant kernel: the one-launch decode step, launch by launch
+    k_us = np.array([[a.elapsed_time(b) * 1000.0 for a, b in kk] for kk in kevs])
+    kernel_us = float(k_us.mean())
+    # its algorithmic bytes: step s + 1 of a generation puts its token at
+    # position 128 + s + 1
+    k_bytes = float(np.mean([decode_bytes_per_step(w, 128 + s) for s in range(1, n_new)]))
+    dec_gbs = k_bytes / (kernel_us * 1e-6) / 1e9
+    traffic = measured_traffic()
 
     # prefill: 1024-token prompt, same shape
     mp = ng.model_from_workload(wp, W, max_batch=1, max_prefill_tokens=1024)
@@ -177,8 +230,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "decode step (one graph launch)"},
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": DECODE_KERNEL,
+                     "kernel_us": round(kernel_us, 2),
+                     "algorithmic_bytes_per_launch": round(k_bytes)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
