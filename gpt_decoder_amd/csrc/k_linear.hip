@@ -75,7 +75,7 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
 // column l % 16 in element i of lane l.  A and B are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int S>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int M,
     int N, int K, EpiArgs e) {
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread (A tile)
   constexpr int BCH = BN * 8 / 256;
+  constexpr uint32_t kOut = 0x80000000u;  // offset past every buffer: reads 0
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS];
 
@@ -105,81 +106,166 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  // Range-checked buffer loads: rows past M / N and K-slabs past K read
+  // zeros, and every load is issued on every path, so the wait before a
+  // stage is used covers exactly that stage.
+  const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(A), (short)0, (int)((uint32_t)M * (uint32_t)lda * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * 2u), 0x00020000);
+  auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  };
+  uint4 ra[S][ACH], rb[S][BCH];
+  auto gload = [&](int st, int k0) {
+    const bool kin = k0 < K;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = m0 + r;
-      ra[i] = row < M ? *reinterpret_cast<const uint4*>(A + (size_t)row * lda + k0 + kc)
-                      : make_uint4(0, 0, 0, 0);
+      const int row = m0 + (c >> 3), kc = (c & 7) * 8;
+      ra[st][i] = ld16(ra_rs, (kin && row < M)
+                                  ? ((uint32_t)row * (uint32_t)lda + (uint32_t)(k0 + kc)) * 2u
+                                  : kOut);
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int c = tid + i * 256;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = n0 + r;
-      rb[i] = row < N ? *reinterpret_cast<const uint4*>(W + (size_t)row * K + k0 + kc)
-                      : make_uint4(0, 0, 0, 0);
+      const int row = n0 + (c >> 3), kc = (c & 7) * 8;
+      rb[st][i] = ld16(rb_rs, (kin && row < N)
+                                  ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + kc)) * 2u
+                                  : kOut);
     }
   };
-  auto sstore = [&](int st) {
+  auto sstore = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(sA[st] + (c >> 3) * LDS + (c & 7) * 8) = ra[i];
+      *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(sB[st] + (c >> 3) * LDS + (c & 7) * 8) = rb[i];
+      *reinterpret_cast<uint4*>(sB[buf] + (c >> 3) * LDS + (c & 7) * 8) = rb[st][i];
     }
   };
 
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int st = it & 1;
-    if (it + 1 < nk) gload((it + 1) * BK);
+  // Epilogue inputs that do not depend on the product are fetched before
+  // the K loop, which hides their latency: the rows' cache positions (QKV)
+  // and, for small tiles, the residual values being added to (RESID).
+  constexpr int kRows = TM * 4;   // output rows of this lane
+  int rpos[kRows], rseq[kRows];
+  constexpr bool kPreRes = (EPI == EPI_RESID) && TM * TN * 4 <= 16;
+  float res[kPreRes ? TM : 1][kPreRes ? TN : 1][4];
+  if constexpr (EPI == EPI_QKV) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sA[st] + r * LDS + kk + (lane >> 4) * 8);
+      for (int v = 0; v < 4; ++v) {
+        const int row = min(m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v, M - 1);
+        rpos[i * 4 + v] = e.row_pos[row];
+        rseq[i * 4 + v] = e.row_b ? e.row_b[row] : row;
       }
+  }
+  if constexpr (kPreRes) {
+    const float* o = static_cast<const float*>(e.out);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 16 + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB[st] + r * LDS + kk + (lane >> 4) * 8);
-      }
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    if (it + 1 < nk) sstore(st ^ 1);
-    __syncthreads();
+        for (int v = 0; v < 4; ++v) {
+          const int row = min(m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v, M - 1);
+          const int col = min(n0 + wn * WN + j * 16 + (lane & 15), N - 1);
+          res[i][j][v] = o[(size_t)row * e.ldo + col];
+        }
   }
 
+  // S K-slabs in flight in registers; slab it goes registers -> LDS buffer
+  // it % 2 -> MFMA.  The trip count is rounded up to a multiple of S (the
+  // extra slabs are zeros).
+  const int nk = K / BK;
+  const int nkp = ((nk + S - 1) / S) * S;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int st = 0; st < S; ++st) gload(st, st * BK);
+  for (int it0 = 0; it0 < nkp; it0 += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const int it = it0 + st;
+      const int buf = st & 1;   // S is even, so it % 2 == st % 2
+      sstore(st, buf);
+      __syncthreads();
+      gload(st, (it + S) * BK);
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 32) {
+        bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * WM + i * 16 + (lane & 15);
+          af[i] = *reinterpret_cast<const bf16x8_t*>(sA[buf] + r * LDS + kk + (lane >> 4) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int r = wn * WN + j * 16 + (lane & 15);
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB[buf] + r * LDS + kk + (lane >> 4) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
+                                                                acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  if constexpr (EPI == EPI_QKV) {
+    // column -> q / k / v, head, dim once per column fragment
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * WN + j * 16 + (lane & 15);
       if (col >= N) continue;
+      const int which = col / e.C;
+      const int c = col - which * e.C;
+      const int hh = c / e.hs, d = c - hh * e.hs;
+      const float bv = e.bias ? to_f32(static_cast<const bf16_t*>(e.bias)[col]) : 0.f;
+      bf16_t* cache = static_cast<bf16_t*>(which == 1 ? e.kc : e.vc);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
-        if (row < M) epi_apply<bf16_t, EPI>(e, row, col, acc[i][j][v]);
-      }
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+          if (row >= M) continue;
+          const bf16_t val = f32_to_bf16(e.bias ? acc[i][j][v] + bv : acc[i][j][v]);
+          if (which == 0) {
+            static_cast<bf16_t*>(e.out)[(size_t)row * e.ldo + c] = val;
+          } else {
+            const int pp = rpos[i * 4 + v];
+            if (pp >= 0)
+              cache[(((size_t)rseq[i * 4 + v] * e.H + hh) * e.Tb + pp) * e.hs + d] = val;
+          }
+        }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WN + j * 16 + (lane & 15);
+        if (col >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+          if (row >= M) continue;
+          if constexpr (kPreRes) {
+            float val = acc[i][j][v];
+            if (e.bias) val += to_f32(static_cast<const bf16_t*>(e.bias)[col]);
+            static_cast<float*>(e.out)[(size_t)row * e.ldo + col] = res[i][j][v] + val;
+          } else {
+            epi_apply<bf16_t, EPI>(e, row, col, acc[i][j][v]);
+          }
+        }
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -607,15 +693,18 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
   if (dtype == NGPT_BF16) {
     const bf16_t* a = static_cast<const bf16_t*>(A);
     const bf16_t* w = static_cast<const bf16_t*>(W);
-    // largest tile that still gives every CU at least one workgroup
+    // Tile size: a workgroup's time is set by the operand bytes it streams,
+    // (BM + BN) * K, and the grid runs in rounds of one workgroup per CU;
+    // pick the smaller rounds * (BM + BN), 128x64 on a tie.
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    constexpr int kCUs = 256;
-    if (M > 64 && tiles(128, 128) >= kCUs)
-      gemm_mfma_kernel<128, 128, EPI><<<tiles(128, 128), 256, 0, s>>>(a, lda, w, M, N, K, e);
-    else if (M > 64 && tiles(128, 64) >= kCUs)
-      gemm_mfma_kernel<128, 64, EPI><<<tiles(128, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
+    auto cost = [&](int bm, int bn) {
+      constexpr int kCUs = 256;
+      return ((tiles(bm, bn) + kCUs - 1) / kCUs) * (bm + bn);
+    };
+    if (M > 64 && cost(128, 64) <= cost(64, 64))
+      gemm_mfma_kernel<128, 64, EPI, 4><<<tiles(128, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
     else
-      gemm_mfma_kernel<64, 64, EPI><<<tiles(64, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
+      gemm_mfma_kernel<64, 64, EPI, 8><<<tiles(64, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
   } else {
     const dim3 grid((N + 15) / 16, (M + 15) / 16);
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(static_cast<const float*>(A), lda,
