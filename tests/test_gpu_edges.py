@@ -279,3 +279,48 @@ def test_fused_greedy_step_matches_sampler_head_node():
         if s % 5 == 2 or s == 25:
             continue
         assert g_ids[s] == int(np.argmax(g_lg[s - 1]))
+
+
+@pytest.mark.parametrize("L,H,C,Tb,plen,steps", [
+    (2, 1, 64, 512, 300, 6),     # one head; three attention items per head
+    (1, 8, 512, 1024, 1000, 6),  # eight items per head near the block end
+    (3, 12, 768, 1024, 1015, 8),  # GPT-2 width, positions up to 1022
+    (2, 4, 256, 64, 10, 40),     # short block, decoded up to its limit
+])
+def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps):
+    """Batch-1 bf16 decode with hs 64 runs as one launch per token.  Its
+    work split depends on the shape and the position (row pairs per
+    workgroup, attention items per head and their XCD placement, record
+    merging, over-read slack at the end of each exchange buffer).  Fed
+    steps and then greedy steps (which fold the argmax into the launch)
+    are checked against the oracle's KV-cached decode of the same ids."""
+    torch = need_gpu()
+    V = 500
+    w = synth.Workload(f"persist_{L}_{H}_{C}_{Tb}", 11, L, H, C, Tb, V, V, False,
+                       "bf16", batch=1, prompt_len=plen)
+    W = synth.make_weights(w, gamma_std=0.1)
+    rng = np.random.default_rng(C + Tb)
+    ids = rng.integers(0, V, (1, plen)).astype(np.int32)
+    feed = rng.integers(0, V, (steps,)).astype(np.int32)
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(1)
+    o = oracle.OracleGPT(w, W, act_bf16=True)
+    worst = max_abs(gpu_prefill(m, kv, ids, [plen]), o.prefill(ids, [plen]))
+    n_feed = min(steps, Tb - plen) // 2
+    for s in range(n_feed):
+        m.decode_feed(kv, dev_i32(feed[s:s + 1]))
+        worst = max(worst, max_abs(m.logits(1).cpu().numpy(), o.decode([int(feed[s])])))
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    prev = m.logits(1).cpu().numpy()
+    for s in range(n_feed, min(steps, Tb - plen)):
+        m.decode_step(kv, nxt, None)
+        tok = int(nxt.cpu().numpy()[0])
+        assert tok == int(np.argmax(prev[0]))
+        prev = m.logits(1).cpu().numpy()
+        worst = max(worst, max_abs(prev, o.decode([tok])))
+    assert m.device_status() == 0
+    assert int(kv.lens.cpu().numpy()[0]) == plen + min(steps, Tb - plen)
+    log(f"  L={L} H={H} C={C} Tb={Tb} p0={plen}: max logit err {worst:.2e}")
+    assert worst < TOL_BF16
+    m.close()
