@@ -81,14 +81,23 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int last_key = min(q0 + 63, len - 1);
+  const int nkt = last_key / KT + 1;   // key tiles this query tile meets
   // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
   // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
-  // The next tile's items are loaded into registers while the current tile
-  // is multiplied.
+  // S tiles are in flight in registers.  The loads are range-checked buffer
+  // loads issued on every path: keys at or past len (whose cache rows may
+  // hold anything) and tiles past the block read zeros.
   constexpr int ITEMS = (KT / 2) * (HS / 8);
   constexpr int IPT = (ITEMS + 255) / 256;
-  uint4 rk[IPT][2], rv[IPT][2];
-  auto load_tile = [&](int k0) {
+  constexpr int S = 4;
+  constexpr uint32_t kOut = 0x80000000u;
+  const uint32_t blk = (uint32_t)Tb * HS * 2u;
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(kbase), (short)0, (int)blk, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(vbase), (short)0, (int)blk, 0x00020000);
+  uint4 rk[S][IPT][2], rv[S][IPT][2];
+  auto load_tile = [&](int st, int k0) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int c = tid + it * 256;
@@ -96,24 +105,22 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const int key = k0 + 2 * kp + e2;
-        const bool ok = c < ITEMS && key < len;
-        rk[it][e2] = ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * HS + d0)
-                        : make_uint4(0, 0, 0, 0);
-        rv[it][e2] = ok ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * HS + d0)
-                        : make_uint4(0, 0, 0, 0);
+        const uint32_t off = (c < ITEMS && key < len) ? ((uint32_t)key * HS + d0) * 2u : kOut;
+        rk[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, off, 0, 0));
+        rv[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, off, 0, 0));
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int st) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int c = tid + it * 256;
       if (c >= ITEMS) break;
       const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rk[it][0];
-      *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rk[it][1];
-      const uint32_t a[4] = {rv[it][0].x, rv[it][0].y, rv[it][0].z, rv[it][0].w};
-      const uint32_t b2[4] = {rv[it][1].x, rv[it][1].y, rv[it][1].z, rv[it][1].w};
+      *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rk[st][it][0];
+      *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rk[st][it][1];
+      const uint32_t a[4] = {rv[st][it][0].x, rv[st][it][0].y, rv[st][it][0].z, rv[st][it][0].w};
+      const uint32_t b2[4] = {rv[st][it][1].x, rv[st][it][1].y, rv[st][it][1].z, rv[st][it][1].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // dims d0+2j (low halves) and d0+2j+1 (high halves) of the two keys
@@ -124,12 +131,17 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       }
     }
   };
-  load_tile(0);
-  for (int k0 = 0; k0 <= last_key; k0 += KT) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) load_tile(st, st * KT);
+  for (int t0 = 0; t0 < nkt; t0 += S) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int k0 = (t0 + st) * KT;
     __syncthreads();
-    store_tile();
+    store_tile(st);
     __syncthreads();
-    if (k0 + KT <= last_key) load_tile(k0 + KT);
+    load_tile(st, k0 + S * KT);
+    if (t0 + st >= nkt) continue;   // padding of the last group (uniform)
 
     // S^T for 4 sub-tiles of 16 keys
     f32x4_t s[4];
@@ -154,8 +166,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
         s[t][i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = fmaxf(tmax, lane_xor16(tmax));
+    tmax = fmaxf(tmax, lane_xor32(tmax));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
     float psum = 0.f;
@@ -167,8 +179,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
         s[t][i] = p;
         psum += p;
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum += lane_xor16(psum);
+    psum += lane_xor32(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
@@ -195,6 +207,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
         o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[d], 0, 0, 0);
       }
     }
+  }
   }
 
   if (qrow < len) {

@@ -60,53 +60,6 @@ constexpr int kRec = kHs + 2;    // record: m, l, o[64]
 constexpr int kRecWords = 512;   // most record words one merger reads
 constexpr int kMaxC = 768;
 
-// ---- cross-lane moves ------------------------------------------------------
-// DPP within a row of 16 lanes, the gfx950 permlane swaps across rows.  Each
-// returns the value of the partner lane named in the comment.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_xor1(float v) { return dpp_mov<0xB1>(v); }  // quad_perm 1,0,3,2
-__device__ __forceinline__ float lane_xor2(float v) { return dpp_mov<0x4E>(v); }  // quad_perm 2,3,0,1
-__device__ __forceinline__ float lane_mirror8(float v) { return dpp_mov<0x141>(v); }  // 7 - i in 8
-__device__ __forceinline__ float lane_xor8(float v) { return dpp_mov<0x128>(v); }  // row_ror:8
-__device__ __forceinline__ float lane_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float lane_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-// [a_lo + a_hi | b_lo + b_hi]: lanes 0..31 sum a over the two halves, lanes
-// 32..63 sum b.
-__device__ __forceinline__ float halves_sum2(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Row r of the result sums rows (r & ~1), (r | 1) of a (r even) or of b
-// (r odd): [a0+a1, b0+b1, a2+a3, b2+b3].
-__device__ __forceinline__ float rows_sum2(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// sum over each row of 16 lanes, in every lane of the row (bit-identical:
-// each step adds a symmetric partner)
-__device__ __forceinline__ float row_sum16(float v) {
-  v += lane_xor1(v);
-  v += lane_xor2(v);
-  v += lane_mirror8(v);
-  v += lane_xor8(v);
-  return v;
-}
-__device__ __forceinline__ float wave_sum_all(float v) {
-  v = row_sum16(v);
-  v += lane_xor16(v);
-  v += lane_xor32(v);
-  return v;
-}
-
 // Range-checked buffer loads: a resource over [base, base + bytes); an offset
 // past the end reads zeros.  Used for every prefetch so that no load sits
 // behind a branch (each wavefront issues the same loads on every path, and
