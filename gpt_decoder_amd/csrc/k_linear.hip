@@ -75,7 +75,7 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
 // column l % 16 in element i of lane l.  A and B are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int EPI, int S>
+template <int BM, int BN, int EPI, int S, int NKC = 0>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int M,
     int N, int K, EpiArgs e) {
@@ -183,10 +183,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   // S K-slabs in flight in registers; slab it goes registers -> LDS buffer
   // it % 2 -> MFMA.  The trip count is rounded up to a multiple of S (the
   // extra slabs are zeros).
-  const int nk = K / BK;
+  const int nk = NKC > 0 ? NKC : K / BK;
   const int nkp = ((nk + S - 1) / S) * S;
 #pragma unroll
   for (int st = 0; st < S; ++st) gload(st, st * BK);
+#pragma unroll (NKC > 0 ? 64 : 1)
   for (int it0 = 0; it0 < nkp; it0 += S) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
@@ -701,10 +702,34 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
       constexpr int kCUs = 256;
       return ((tiles(bm, bn) + kCUs - 1) / kCUs) * (bm + bn);
     };
-    if (M > 64 && cost(128, 64) <= cost(64, 64))
-      gemm_mfma_kernel<128, 64, EPI, 4><<<tiles(128, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
-    else
-      gemm_mfma_kernel<64, 64, EPI, 8><<<tiles(64, 64), 256, 0, s>>>(a, lda, w, M, N, K, e);
+    // K-slab counts of the GPT-2-small widths (768 and 4 * 768) are
+    // compile-time constants, so the K loop is fully unrolled: at every trip
+    // of a rolled loop the compiler waits for all loads in flight.
+    const bool big = M > 64 && cost(128, 64) <= cost(64, 64);
+    const int g = big ? tiles(128, 64) : tiles(64, 64);
+    // (only the pairs a block issues: c_attn, c_fc, c_proj at K = 768, the
+    // MLP projection at K = 3072)
+    constexpr bool k768 = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_RESID;
+    constexpr bool k3072 = EPI == EPI_RESID;
+    bool done = false;
+    if constexpr (k768) {
+      if (K == 768) {
+        if (big) gemm_mfma_kernel<128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        done = true;
+      }
+    }
+    if constexpr (k3072) {
+      if (K == 3072) {
+        if (big) gemm_mfma_kernel<128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<64, 64, EPI, 8, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        done = true;
+      }
+    }
+    if (!done) {
+      if (big) gemm_mfma_kernel<128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+    }
   } else {
     const dim3 grid((N + 15) / 16, (M + 15) / 16);
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(static_cast<const float*>(A), lda,
