@@ -94,6 +94,7 @@ struct ngpt_model {
   float* logits = nullptr;
   int32_t *row_b = nullptr, *row_pos = nullptr, *last_rows = nullptr;
   float* part = nullptr;
+  float* ppart = nullptr;   // prefill attention key-split partials (one sequence)
   int32_t *tok = nullptr, *pos = nullptr, *status = nullptr;
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
@@ -216,6 +217,8 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
                o_lg = carve(Bm * (size_t)m->V * 4), o_rb = carve(Mm * 4),
                o_rp = carve(Mm * 4), o_lr = carve(Bm * 4),
                o_part = carve(Bm * m->H * (size_t)m->nchunk * (m->hs + 2) * 4),
+               o_ppart = carve((size_t)m->H * m->Tb * attn_prefill_split_chunks(m->Tb) *
+                               (m->hs + 4) * 4),
                o_tok = carve(Bm * 4),
                o_pos = carve(Bm * 4), o_st = carve(16),
                o_prm = carve(sizeof(SampleParams));
@@ -249,6 +252,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
   m->logits = (float*)(base + o_lg);
   m->row_b = (int32_t*)(base + o_rb); m->row_pos = (int32_t*)(base + o_rp);
   m->last_rows = (int32_t*)(base + o_lr); m->part = (float*)(base + o_part);
+  m->ppart = (float*)(base + o_ppart);
   m->tok = (int32_t*)(base + o_tok);
   m->pos = (int32_t*)(base + o_pos); m->status = (int32_t*)(base + o_st);
   m->params = (SampleParams*)(base + o_prm);
@@ -383,7 +387,7 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
     launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, M, 3 * C, C, eq, s);
     launch_attn_prefill(dt, m->q, C, kl, vl, map, maxlen, m->H, m->hs, m->Tb,
-                        m->y, C, s);
+                        m->y, C, m->ppart, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
     launch_linear(dt, EPI_RESID, m->y, C, nullptr, w.attnproj_w, M, C, C, ep, s);

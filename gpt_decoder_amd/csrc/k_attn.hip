@@ -29,6 +29,7 @@
 namespace ngpt {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPrefillKch = 4;   // key tiles per chunk when a prefill tile is split
 
 // ---------------------------------------------------------------------------
 // Prefill, bf16 MFMA.  Scores are formed transposed, S^T = K Q^T, so that a
@@ -38,11 +39,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 // O^T = V^T P^T; P^T is fed straight from the score registers, with V^T read
 // from a transposed LDS copy in the same key order.
 // ---------------------------------------------------------------------------
+//
+// Key split (kch > 0, batch 1): a query tile that meets more than kch key
+// tiles is split into chunks of kch key tiles, one workgroup each; such a
+// chunk leaves its rows' unnormalised state (m, l, o) in part, and
+// attn_prefill_merge combines the chunks in order.  Workgroup x takes query
+// tile ntiles - 1 - x / nsplit (heavy tiles first) and chunk x % nsplit.
 template <int HS>
 __global__ __launch_bounds__(256) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc,
     const bf16_t* __restrict__ vc, RowMap map, int H, int Tb, float scale,
-    bf16_t* __restrict__ y, int ldy) {
+    bf16_t* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part) {
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = HS + 8;         // sK row stride (elements)
   constexpr int VS = KT + 8;         // sVt row stride (elements)
@@ -54,8 +61,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const int b = blockIdx.z, h = blockIdx.y;
   const int len = map.off[b + 1] - map.off[b];
   const int ntiles = (len + 63) / 64;
-  const int qt = ntiles - 1 - (int)blockIdx.x;  // heavy tiles first
+  const int qt = ntiles - 1 - (kch > 0 ? (int)blockIdx.x / nsplit : (int)blockIdx.x);
   if (qt < 0) return;
+  // key tiles [kt0, kt1) of this workgroup
+  const int nch = kch > 0 ? (qt + kch) / kch : 1;
+  const int chunk = kch > 0 ? (int)blockIdx.x % nsplit : 0;
+  if (chunk >= nch) return;
+  const int kt0 = kch > 0 ? chunk * kch : 0;
   const int q0 = qt * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;                       // lane group 0..3
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int last_key = min(q0 + 63, len - 1);
-  const int nkt = last_key / KT + 1;   // key tiles this query tile meets
+  const int nkt = (nch > 1 ? min(kt0 + kch, qt + 1) : last_key / KT + 1) - kt0;
   // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
   // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
   // S tiles are in flight in registers.  The loads are range-checked buffer
@@ -132,11 +144,11 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     }
   };
 #pragma unroll
-  for (int st = 0; st < S; ++st) load_tile(st, st * KT);
+  for (int st = 0; st < S; ++st) load_tile(st, (kt0 + st) * KT);
   for (int t0 = 0; t0 < nkt; t0 += S) {
 #pragma unroll
   for (int st = 0; st < S; ++st) {
-    const int k0 = (t0 + st) * KT;
+    const int k0 = (kt0 + t0 + st) * KT;
     __syncthreads();
     store_tile(st);
     __syncthreads();
@@ -210,6 +222,18 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   }
   }
 
+  if (nch > 1) {   // a chunk of a split tile: leave (m, l, o) for the merge
+    if (qrow < len) {
+      // record: m, l, 2 spare, o[HS] (16-byte aligned)
+      float* pp = part + (((size_t)h * Tb + qrow) * nsplit + chunk) * (HS + 4);
+      if (g == 0) { pp[0] = m_run; pp[1] = l_run; }
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+        *reinterpret_cast<float4*>(pp + 4 + d * 16 + g * 4) =
+            make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+    }
+    return;
+  }
   if (qrow < len) {
     const float inv = 1.f / l_run;
     bf16_t* yp = y + (row0 + qrow) * ldy + h * HS;
@@ -220,6 +244,24 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       *reinterpret_cast<uint2*>(yp + d * 16 + g * 4) = make_uint2(w0, w1);
     }
   }
+}
+
+// Merge of a split query tile's chunks (batch 1): one wavefront per (row,
+// head); lane d merges dimension d over the chunks in chunk order.
+template <int HS>
+__global__ __launch_bounds__(64) void attn_prefill_merge(const float* __restrict__ part,
+                                                         int len, int Tb, int kch, int nsplit,
+                                                         bf16_t* __restrict__ y, int ldy) {
+  const int row = kch * 64 + (int)blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  if (row >= len || d >= HS) return;
+  const int nch = (row / 64 + kch) / kch;
+  const float* pp = part + ((size_t)h * Tb + row) * nsplit * (HS + 4);
+  float m = pp[0], l = pp[1], o = pp[4 + d];
+  for (int c = 1; c < nch; ++c) {
+    const float* pc = pp + c * (HS + 4);
+    merge_state(m, l, &o, pc[0], pc[1], &pc[4 + d], 1);
+  }
+  y[(size_t)row * ldy + h * HS + d] = f32_to_bf16(o / l);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,20 +453,35 @@ __global__ __launch_bounds__(64) void attn_decode_combine(
 }
 
 // ---------------------------------------------------------------------------
+int attn_prefill_split_chunks(int Tb) { return ((Tb + 63) / 64 + kPrefillKch - 1) / kPrefillKch; }
+
 void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
                          const void* vc, const RowMap& map, int maxlen, int H,
-                         int hs, int Tb, void* y, int ldy, hipStream_t s) {
+                         int hs, int Tb, void* y, int ldy, float* part, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hs);
-  const dim3 grid((maxlen + 63) / 64, H, map.B);
+  const int ntiles = (maxlen + 63) / 64;
   if (dtype == NGPT_BF16) {
     const bf16_t* qq = (const bf16_t*)q;
+    // one sequence with few workgroups: split the long query tiles' keys
+    const bool split = part && map.B == 1 && ntiles > kPrefillKch && ntiles * H < 256;
+    const int kch = split ? kPrefillKch : 0;
+    const int nsplit = split ? (ntiles + kPrefillKch - 1) / kPrefillKch : 1;
+    const dim3 grid(ntiles * nsplit, H, map.B);
     if (hs == 64)
       attn_prefill_mfma<64><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
-          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy);
+          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
     else
       attn_prefill_mfma<32><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
-          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy);
+          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
+    if (split) {
+      const dim3 mgrid(maxlen - kch * 64, H);
+      if (hs == 64)
+        attn_prefill_merge<64><<<mgrid, 64, 0, s>>>(part, maxlen, Tb, kch, nsplit, (bf16_t*)y, ldy);
+      else
+        attn_prefill_merge<32><<<mgrid, 64, 0, s>>>(part, maxlen, Tb, kch, nsplit, (bf16_t*)y, ldy);
+    }
   } else {
+    const dim3 grid(ntiles, H, map.B);
     const float* qq = (const float*)q;
     if (hs == 64)
       attn_prefill_simt<float, 64><<<grid, 64, 0, s>>>(qq, ldq, (const float*)kc,

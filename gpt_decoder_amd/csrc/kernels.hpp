@@ -91,7 +91,10 @@ void launch_linear(int dtype, int epi, const void* A, int lda,
 // j*hs), the output y [M][ldy] likewise.
 void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
                          const void* vc, const RowMap& map, int maxlen, int H,
-                         int hs, int Tb, void* y, int ldy, hipStream_t s);
+                         int hs, int Tb, void* y, int ldy, float* part, hipStream_t s);
+// chunks per (row, head) of the prefill key split: the partial buffer holds
+// [H][Tb][chunks][hs + 4] floats (one sequence)
+int attn_prefill_split_chunks(int Tb);
 
 // One query per active sequence (pos[b] >= 0) against cache rows
 // 0..pos[b], split over key chunks: each chunk leaves a record (max, sum,
@@ -143,7 +146,7 @@ void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
 void launch_sampler(const SamplerArgs& a, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// One-launch decode step for batch 1 (bf16, head size 64, n_embd <= 1024).
+// One-launch decode step for batch 1 (bf16, head size 64, n_embd <= 768).
 struct PersistLayer {
   const bf16_t *ln1_w, *ln1_b, *attn_w, *attn_b, *proj_w, *proj_b;
   const bf16_t *ln2_w, *ln2_b, *fc_w, *fc_b, *mp_w, *mp_b;
