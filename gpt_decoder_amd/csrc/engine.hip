@@ -99,7 +99,7 @@ struct ngpt_model {
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
   // one-launch batch-1 decode (see k_persist.hip)
-  int grid_cus = 0;
+  int persist_grid = 0;   // workgroups of the one-launch decode kernel
   bool persist = false;
   PersistLayer* d_layers = nullptr;
   uint64_t *e_qkv = nullptr, *e_rec = nullptr, *e_y = nullptr, *e_x1 = nullptr,
@@ -229,8 +229,16 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
     if (hipGetDevice(&dev) == hipSuccess)
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   }
-  m->grid_cus = cus;
-  m->persist = persistent_decode_supported(cfg->dtype, m->C, m->H, m->L, m->Tb, 1, cus);
+  // One-launch decode grid: the fewest workgroups (a multiple of 8, at most
+  // one per CU) whose register slabs hold every phase's rows.  Each exchange
+  // waits for words from all workgroups, and that wait shortens with fewer
+  // participants (measured: 245 us per GPT-2-small step at 192 workgroups,
+  // 260 at 224, 265 at 256).
+  int pgrid = 0;
+  for (int g = 64; g <= cus && pgrid == 0; g += 8)
+    if (persistent_decode_supported(cfg->dtype, m->C, m->H, m->L, m->Tb, 1, g)) pgrid = g;
+  m->persist_grid = pgrid;
+  m->persist = pgrid > 0;
   const size_t L = m->L, SL = (size_t)persistent_exchange_slack();
   const size_t o_eq = m->persist ? carve((L * 3 * C + SL) * 8) : 0,
                o_er = m->persist ? carve((L * m->H * (size_t)m->nchunk * (m->hs + 2) + SL) * 8) : 0,
@@ -239,7 +247,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
                o_ef = m->persist ? carve((L * 4 * C + SL) * 8) : 0,
                o_e2 = m->persist ? carve((L * C + SL) * 8) : 0,
                o_ep = m->persist ? carve(16) : 0,
-               o_ec = m->persist ? carve((2 * (size_t)cus + SL) * 8) : 0,
+               o_ec = m->persist ? carve((2 * (size_t)pgrid + SL) * 8) : 0,
                o_dl = m->persist ? carve(L * sizeof(PersistLayer)) : 0;
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
@@ -440,7 +448,7 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
   if (m->persist && Bk == 1) {
-    launch_decode_persistent(persist_args(m, kv), m->grid_cus, s);
+    launch_decode_persistent(persist_args(m, kv), m->persist_grid, s);
     return;
   }
   for (int l = 0; l < m->L; ++l) {
@@ -550,7 +558,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
     PersistArgs a = persist_args(m, kv);
     a.fused = 1;
     a.next_ids = arg_out;
-    launch_decode_persistent(a, m->grid_cus, m->stream);
+    launch_decode_persistent(a, m->persist_grid, m->stream);
     HIP_TRY(m, hipGetLastError());
     if (m->h_lens[0] < m->h_limit[0]) ++m->h_lens[0];
     return NGPT_OK;
