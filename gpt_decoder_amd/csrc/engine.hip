@@ -182,7 +182,7 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
   const bool bias = cfg->bias != 0;
   if ((w->lnf_b != nullptr) != bias)
     return fail(nullptr, NGPT_E_ARG, "lnf_b must be non-NULL iff bias");
-  if (misaligned(w->wte) || misaligned(w->wpe))
+  if (misaligned(w->wte) || misaligned(w->wpe) || misaligned(w->lnf_w) || misaligned(w->lnf_b))
     return fail(nullptr, NGPT_E_ARG, "weights must be 16-byte aligned");
   for (int l = 0; l < cfg->n_layer; ++l) {
     const ngpt_layer_weights& lw = w->layers[l];
@@ -192,9 +192,11 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
       if (!p) return fail(nullptr, NGPT_E_ARG, "missing layer weight pointer");
       if (misaligned(p)) return fail(nullptr, NGPT_E_ARG, "weights must be 16-byte aligned");
     }
-    for (const void* p : opt)
+    for (const void* p : opt) {
       if ((p != nullptr) != bias)
         return fail(nullptr, NGPT_E_ARG, "bias pointers must be non-NULL iff bias");
+      if (misaligned(p)) return fail(nullptr, NGPT_E_ARG, "weights must be 16-byte aligned");
+    }
   }
 
   ngpt_model* m = new ngpt_model();

@@ -73,6 +73,27 @@ __global__ __launch_bounds__(256) void embed_decode_kernel(
 // once and every load is issued before the first reduction.
 constexpr int kLnMaxVec = 8;  // C <= 2048
 
+// Four consecutive elements at a multiple of 4 (C is a multiple of 32 and
+// the parameter and output rows are 16-byte aligned), so the LayerNorm
+// parameters are read and its output written with one access per lane.
+__device__ __forceinline__ void load4(const bf16_t* p, float* f) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  f[0] = to_f32(static_cast<bf16_t>(u.x & 0xffffu));
+  f[1] = to_f32(static_cast<bf16_t>(u.x >> 16));
+  f[2] = to_f32(static_cast<bf16_t>(u.y & 0xffffu));
+  f[3] = to_f32(static_cast<bf16_t>(u.y >> 16));
+}
+__device__ __forceinline__ void load4(const float* p, float* f) {
+  const float4 t = *reinterpret_cast<const float4*>(p);
+  f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+}
+__device__ __forceinline__ void store4(bf16_t* p, const float* f) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+}
+__device__ __forceinline__ void store4(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const float* __restrict__ x, int ldx, const int32_t* __restrict__ rows,
@@ -109,12 +130,15 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
     const int c = j * 256 + lane * 4;
     if (c < C) {
       const float xv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      float wv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
+      load4(w + c, wv);
+      if (bias) load4(bias + c, bv);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        float y = (xv[u] - mean) * rstd * to_f32(w[c + u]);
-        if (bias) y += to_f32(bias[c + u]);
-        o[c + u] = from_f32<T>(y);
+        y[u] = (xv[u] - mean) * rstd * wv[u];
+        if (bias) y[u] += bv[u];
       }
+      store4(o + c, y);
     }
   }
 }

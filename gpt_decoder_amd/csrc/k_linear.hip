@@ -57,6 +57,28 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
   }
 }
 
+// Bias of four consecutive output columns col .. col + 3 (the MFMA kernel's
+// bf16 epilogues), by value so that nothing goes to scratch; columns at or
+// past N get none.
+__device__ __forceinline__ float4 add_bias4(const bf16_t* b, int col, int N, float4 v) {
+  if (col + 3 < N) {
+    const uint2 u = *reinterpret_cast<const uint2*>(b + col);
+    v.x += to_f32(static_cast<bf16_t>(u.x & 0xffffu));
+    v.y += to_f32(static_cast<bf16_t>(u.x >> 16));
+    v.z += to_f32(static_cast<bf16_t>(u.y & 0xffffu));
+    v.w += to_f32(static_cast<bf16_t>(u.y >> 16));
+  } else {
+    v.x += to_f32(b[col]);
+    if (col + 1 < N) v.y += to_f32(b[col + 1]);
+    if (col + 2 < N) v.z += to_f32(b[col + 2]);
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
+  return make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA tile GEMM.  256 threads = 4 wavefronts in a 2x2 arrangement; each
 // wavefront owns a (BM/2) x (BN/2) sub-tile built from 16x16 MFMA tiles.  K is
@@ -70,9 +92,15 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
 // weight panel run back to back on the same L2.
 //
 // MFMA operand layout used (v_mfma_f32_16x16x32_bf16): lane l supplies row
-// (l % 16) of A and column (l % 16) of B, each as 8 consecutive K values
-// starting at 8 * (l / 16); the 16x16 fp32 result holds row 4 * (l / 16) + i,
-// column l % 16 in element i of lane l.  A and B are fed with the same K
+// (l % 16) of the first operand and column (l % 16) of the second, each as 8
+// consecutive K values starting at 8 * (l / 16); the 16x16 fp32 result holds
+// row 4 * (l / 16) + i, column l % 16 in element i of lane l.  For the bf16
+// outputs (q/k/v, GELU, plain store) the weight fragment goes first: each
+// 16x16 result is then a tile of (A W^T)^T, and lane l holds output row
+// (l % 16) at four consecutive columns, written with one 8-byte store.  For
+// the fp32 outputs (residual add, logits) the A fragment goes first, and 16
+// lanes cover 16 consecutive columns of a row (measured faster for the
+// read-modify-write of the residual).  Both operands are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int EPI, int S, int NKC = 0>
@@ -86,6 +114,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread (A tile)
   constexpr int BCH = BN * 8 / 256;
   constexpr uint32_t kOut = 0x80000000u;  // offset past every buffer: reads 0
+  // weight fragment first for the bf16-output epilogues (see the epilogue)
+  constexpr bool kSwap = (EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_STORE);
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS];
 
@@ -152,19 +182,21 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   // Epilogue inputs that do not depend on the product are fetched before
   // the K loop, which hides their latency: the rows' cache positions (QKV)
   // and, for small tiles, the residual values being added to (RESID).
-  constexpr int kRows = TM * 4;   // output rows of this lane
-  int rpos[kRows], rseq[kRows];
+  // (kSwap: lane l holds output row (l % 16) of each row fragment at the
+  // four consecutive columns 4 * (l / 16) + i of each column fragment;
+  // otherwise column (l % 16) at rows 4 * (l / 16) + i)
+  auto out_row = [&](int i) { return m0 + wm * WM + i * 16 + (lane & 15); };
+  auto out_col = [&](int j) { return n0 + wn * WN + j * 16 + (lane >> 4) * 4; };
+  int rpos[TM], rseq[TM];
   constexpr bool kPreRes = (EPI == EPI_RESID) && TM * TN * 4 <= 16;
   float res[kPreRes ? TM : 1][kPreRes ? TN : 1][4];
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = min(m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v, M - 1);
-        rpos[i * 4 + v] = e.row_pos[row];
-        rseq[i * 4 + v] = e.row_b ? e.row_b[row] : row;
-      }
+    for (int i = 0; i < TM; ++i) {
+      const int row = min(out_row(i), M - 1);
+      rpos[i] = e.row_pos[row];
+      rseq[i] = e.row_b ? e.row_b[row] : row;
+    }
   }
   if constexpr (kPreRes) {
     const float* o = static_cast<const float*>(e.out);
@@ -213,39 +245,62 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
-                                                                acc[i][j], 0, 0, 0);
+            acc[i][j] = kSwap ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i],
+                                                                        acc[i][j], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
+                                                                        acc[i][j], 0, 0, 0);
       }
     }
   }
 
   if constexpr (EPI == EPI_QKV) {
-    // column -> q / k / v, head, dim once per column fragment
+    // columns -> q / k / v, head, dim once per column fragment (the four
+    // columns of a lane lie in one head: 4 | hs, and 4 | ldo = n_embd)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + j * 16 + (lane & 15);
+      const int col = out_col(j);
       if (col >= N) continue;
       const int which = col / e.C;
       const int c = col - which * e.C;
       const int hh = c / e.hs, d = c - hh * e.hs;
-      const float bv = e.bias ? to_f32(static_cast<const bf16_t*>(e.bias)[col]) : 0.f;
       bf16_t* cache = static_cast<bf16_t*>(which == 1 ? e.kc : e.vc);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
-          if (row >= M) continue;
-          const bf16_t val = f32_to_bf16(e.bias ? acc[i][j][v] + bv : acc[i][j][v]);
-          if (which == 0) {
-            static_cast<bf16_t*>(e.out)[(size_t)row * e.ldo + c] = val;
-          } else {
-            const int pp = rpos[i * 4 + v];
-            if (pp >= 0)
-              cache[(((size_t)rseq[i * 4 + v] * e.H + hh) * e.Tb + pp) * e.hs + d] = val;
-          }
+      for (int i = 0; i < TM; ++i) {
+        const int row = out_row(i);
+        if (row >= M) continue;
+        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (e.bias) v = add_bias4(static_cast<const bf16_t*>(e.bias), col, N, v);
+        const uint2 packed = pack_bf16x4(v);
+        if (which == 0) {
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(e.out) + (size_t)row * e.ldo + c) = packed;
+        } else if (rpos[i] >= 0) {
+          *reinterpret_cast<uint2*>(
+              cache + (((size_t)rseq[i] * e.H + hh) * e.Tb + rpos[i]) * e.hs + d) = packed;
         }
+      }
     }
+  } else if constexpr (kSwap) {  // EPI_GELU, EPI_STORE: bf16 rows
+    const bool vec = (e.ldo & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = out_row(i), col = out_col(j);
+        if (row >= M || col >= N) continue;
+        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (e.bias) v = add_bias4(static_cast<const bf16_t*>(e.bias), col, N, v);
+        if constexpr (EPI == EPI_GELU)
+          v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
+        bf16_t* o = static_cast<bf16_t*>(e.out) + (size_t)row * e.ldo + col;
+        if (vec && col + 3 < N) {
+          *reinterpret_cast<uint2*>(o) = pack_bf16x4(v);
+        } else {
+          o[0] = f32_to_bf16(v.x);
+          if (col + 1 < N) o[1] = f32_to_bf16(v.y);
+          if (col + 2 < N) o[2] = f32_to_bf16(v.z);
+          if (col + 3 < N) o[3] = f32_to_bf16(v.w);
+        }
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i)

@@ -145,8 +145,12 @@ int ngpt_check_config(const ngpt_config *cfg);
  * (NULL = the default stream) on which every later call enqueues its work.
  * Allocates the workspace (activations, split-K partials, fp32 logits
  * [max_batch][vocab]).  Sampling defaults: greedy.
+ * Every weight and bias pointer must be 16-byte aligned (the kernels read
+ * parameter rows with 8- and 16-byte accesses); fresh device allocations and
+ * framework tensors are.
  * Errors: NGPT_E_ARG (NULL pointers, bias pointers inconsistent with
- * cfg->bias), NGPT_E_CONFIG, NGPT_E_HIP.  *out is NULL on error.
+ * cfg->bias, misaligned pointers), NGPT_E_CONFIG, NGPT_E_HIP.  *out is NULL
+ * on error.
  */
 int ngpt_create(const ngpt_config *cfg, const ngpt_weights *w, void *stream,
                 ngpt_model **out);
