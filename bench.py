@@ -26,7 +26,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
 DECODE_KERNEL = "decode_persistent_kernel"
-KERNEL_SOURCE = os.path.join(ROOT, "gpt_decoder_amd", "csrc", "k_persist.hip")
+# the decode kernel's sources and the file that picks its launch grid: the
+# counter summary is valid only for exactly these
+KERNEL_SOURCES = [os.path.join(ROOT, "gpt_decoder_amd", "csrc", f)
+                  for f in ("k_persist.hip", "common.hpp", "kernels.hpp", "engine.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_persistent_gpt2_124m_b1_traffic.txt")
 
 
@@ -41,16 +44,24 @@ def decode_bytes_per_step(w, pos: int) -> int:
     return weights + ln + kv
 
 
+def kernel_sources_sha256() -> str:
+    """SHA-256 over the decode kernel's sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the decode kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
     calibration), or None when that summary was taken on a different
-    version of the kernel source."""
-    import hashlib
+    version of the kernel's sources."""
     try:
         fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
                       if ":" in line)
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        src = kernel_sources_sha256()
         if fields.get("kernel_source_sha256", "").strip() != src:
             return None
         return float(fields["traffic_bytes_per_launch"])
