@@ -777,7 +777,7 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
     if constexpr (k3072) {
       if (K == 3072) {
         if (big) gemm_mfma_kernel<128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        else gemm_mfma_kernel<64, 64, EPI, 8, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<64, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
         done = true;
       }
     }
