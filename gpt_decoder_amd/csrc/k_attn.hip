@@ -247,12 +247,15 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 }
 
 // Merge of a split query tile's chunks (batch 1): one wavefront per (row,
-// head); lane d merges dimension d over the chunks in chunk order.
+// head), four rows per workgroup; lane d merges dimension d over the chunks
+// in chunk order.
+constexpr int kMergeRows = 4;
 template <int HS>
-__global__ __launch_bounds__(64) void attn_prefill_merge(const float* __restrict__ part,
-                                                         int len, int Tb, int kch, int nsplit,
-                                                         bf16_t* __restrict__ y, int ldy) {
-  const int row = kch * 64 + (int)blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(64 * kMergeRows) void attn_prefill_merge(
+    const float* __restrict__ part, int len, int Tb, int kch, int nsplit,
+    bf16_t* __restrict__ y, int ldy) {
+  const int row = kch * 64 + (int)blockIdx.x * kMergeRows + (int)(threadIdx.x >> 6);
+  const int h = blockIdx.y, d = threadIdx.x & 63;
   if (row >= len || d >= HS) return;
   const int nch = (row / 64 + kch) / kch;
   const float* pp = part + ((size_t)h * Tb + row) * nsplit * (HS + 4);
@@ -474,11 +477,13 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
       attn_prefill_mfma<32><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
           (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
     if (split) {
-      const dim3 mgrid(maxlen - kch * 64, H);
+      const dim3 mgrid((maxlen - kch * 64 + kMergeRows - 1) / kMergeRows, H);
       if (hs == 64)
-        attn_prefill_merge<64><<<mgrid, 64, 0, s>>>(part, maxlen, Tb, kch, nsplit, (bf16_t*)y, ldy);
+        attn_prefill_merge<64><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, Tb, kch, nsplit,
+                                                                (bf16_t*)y, ldy);
       else
-        attn_prefill_merge<32><<<mgrid, 64, 0, s>>>(part, maxlen, Tb, kch, nsplit, (bf16_t*)y, ldy);
+        attn_prefill_merge<32><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, Tb, kch, nsplit,
+                                                                (bf16_t*)y, ldy);
     }
   } else {
     const dim3 grid(ntiles, H, map.B);
