@@ -1,6 +1,7 @@
 // One-launch decode step for a single sequence (batch 1, bf16, head size
 // 64): the whole one-token forward of every block plus ln_f and the tied
-// lm_head, in one persistent kernel with one workgroup per CU.
+// lm_head, in one persistent kernel with at most one workgroup per CU (the
+// host picks the fewest workgroups whose register slabs hold a phase's rows).
 //
 // The arithmetic is the same as the per-layer kernels' (pre-LN block of the
 // architecture analysis "nanoGPT 架构分析", section 4.1; KV-cached attention of

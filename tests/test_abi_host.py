@@ -105,6 +105,20 @@ def test_create_rejects_bad_arguments_before_any_device_work():
     wt = ng.binding.Weights(4096 + 2, 4096, 4096, 0, layers)
     rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG
+    # misaligned lnf_w (the LayerNorm kernels read parameters 4 at a time)
+    wt = ng.binding.Weights(4096, 4096, 4096 + 4, 0, layers)
+    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
+    assert rc == ng.NGPT_E_ARG and b"aligned" in lib.ngpt_last_error(None)
+    # misaligned bias pointer on a model with biases
+    bcfg = cfg_of(w, bias=1)
+    blayers = (ng.binding.LayerWeights * w.n_layer)()
+    for l in range(w.n_layer):
+        for f in ng.binding._LAYER_FIELDS:
+            setattr(blayers[l], f, 4096)
+    blayers[2].fc_b = 4096 + 8
+    wt = ng.binding.Weights(4096, 4096, 4096, 4096, blayers)
+    rc = lib.ngpt_create(ctypes.byref(bcfg), ctypes.byref(wt), None, ctypes.byref(out))
+    assert rc == ng.NGPT_E_ARG and b"aligned" in lib.ngpt_last_error(None)
     # missing layer weight
     layers[1].fc_w = 0
     wt = ng.binding.Weights(4096, 4096, 4096, 0, layers)
