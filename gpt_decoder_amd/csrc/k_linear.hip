@@ -217,9 +217,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   // extra slabs are zeros).
   const int nk = NKC > 0 ? NKC : K / BK;
   const int nkp = ((nk + S - 1) / S) * S;
+  constexpr int kUnroll = NKC > 0 ? 64 : 1;   // whole loop when K is known
 #pragma unroll
   for (int st = 0; st < S; ++st) gload(st, st * BK);
-#pragma unroll (NKC > 0 ? 64 : 1)
+#pragma unroll kUnroll
   for (int it0 = 0; it0 < nkp; it0 += S) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
