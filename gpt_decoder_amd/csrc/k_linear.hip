@@ -22,6 +22,7 @@
 namespace ngpt {
 
 constexpr int kGemvMaxRows = 4;  // rows handled by the streaming kernels
+constexpr int kGemvLnMaxK = 2048;  // widest row the fused LayerNorm holds (n_embd limit)
 
 template <class T, int EPI>
 __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
@@ -689,14 +690,19 @@ static void launch_gemv_c(const T* A, int lda, const LnArgs& ln, const T* W,
   constexpr int SPAN = 64 * (16 / sizeof(T));
   const int nch = (K + SPAN - 1) / SPAN;
   const int grid = (N + CPW - 1) / CPW;
-  if (nch <= 2)
+  // with a fused LayerNorm (K = n_embd <= kGemvLnMaxK) only the chunk counts
+  // that K can need are built: the larger ones would not fit in registers
+  constexpr int kMaxNch = LN ? kGemvLnMaxK / SPAN : 16;
+  if (nch <= 2) {
     gemv_kernel<T, EPI, MR, CPW, 2, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
-  else if (nch <= 4)
+  } else if (nch <= 4) {
     gemv_kernel<T, EPI, MR, CPW, 4, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
-  else if (nch <= 8)
-    gemv_kernel<T, EPI, MR, CPW, 8, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
-  else
-    gemv_kernel<T, EPI, MR, CPW, 16, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+  } else if constexpr (kMaxNch >= 8) {
+    if (nch <= 8)
+      gemv_kernel<T, EPI, MR, CPW, 8, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+    else if constexpr (kMaxNch >= 16)
+      gemv_kernel<T, EPI, MR, CPW, 16, LN><<<grid, 64, 0, s>>>(A, lda, ln, W, M, N, K, e);
+  }
 }
 
 template <class T, int EPI, int MR, bool LN>
@@ -728,7 +734,10 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
                      const void* W, int M, int N, int K, const EpiArgs& e,
                      hipStream_t s) {
   const LnArgs none{};
-  if (M <= kGemvMaxRows) {
+  // streaming path: up to 16 chunks of 64 16-byte vectors per row (K <= 8192
+  // bf16 / 4096 fp32), with a fused LayerNorm only up to kGemvLnMaxK
+  const int gemv_max_k = 16 * 64 * (dtype == NGPT_BF16 ? 8 : 4);
+  if (M <= kGemvMaxRows && K <= gemv_max_k && (!ln || K <= kGemvLnMaxK)) {
     if (dtype == NGPT_BF16) {
       const bf16_t* a = static_cast<const bf16_t*>(A);
       const bf16_t* w = static_cast<const bf16_t*>(W);

@@ -324,3 +324,33 @@ def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps):
     log(f"  L={L} H={H} C={C} Tb={Tb} p0={plen}: max logit err {worst:.2e}")
     assert worst < TOL_BF16
     m.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B", [1, 3])
+def test_fp32_rows_wider_than_the_streaming_kernel(B):
+    """fp32 model with n_embd = 1280: the MLP projection's K = 5120 is wider
+    than one streaming (GEMV) launch covers for fp32 (16 chunks of 256), so
+    these small-batch rows take the tiled kernel.  Ragged prefill and fed
+    decode steps match the oracle at the fp32 bar."""
+    need_gpu()
+    V = 65
+    w = synth.Workload("fp32_wide_1280", 12, 1, 20, 1280, 16, V, V, False, "f32",
+                       batch=B, prompt_len=6)
+    W = synth.make_weights(w)
+    rng = np.random.default_rng(1280 + B)
+    ids = rng.integers(0, V, (B, 6)).astype(np.int32)
+    lens = [6 - b for b in range(B)]
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(B)
+    o = oracle.OracleGPT(w, W, act_bf16=False)
+    worst = max_abs(gpu_prefill(m, kv, ids, lens), o.prefill(ids, lens))
+    for s in range(4):
+        tok = rng.integers(0, V, (B,)).astype(np.int32)
+        m.decode_feed(kv, dev_i32(tok))
+        worst = max(worst, max_abs(m.logits(B).cpu().numpy(), o.decode([int(t) for t in tok])))
+    assert m.device_status() == 0
+    log(f"  fp32 C=1280 B={B}: max logit err {worst:.2e}")
+    assert worst < TOL_F32
+    m.close()
