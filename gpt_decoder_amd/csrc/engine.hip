@@ -143,6 +143,16 @@ static int check_config(const ngpt_config* c, std::string* why) {
   if (c->bias != 0 && c->bias != 1) return bad("bias must be 0 or 1");
   if (c->max_batch < 1 || c->max_batch > NGPT_MAX_BATCH) return bad("max_batch must be in [1, NGPT_MAX_BATCH]");
   if (c->max_prefill_tokens < 1) return bad("max_prefill_tokens must be >= 1");
+  // The kernels address each matrix with 32-bit buffer offsets and use
+  // offset 2^31 as "past the end" (reads zeros), so every weight matrix and
+  // every activation buffer must stay below 2 GiB.
+  const size_t esz = c->dtype == NGPT_BF16 ? 2 : 4;
+  const size_t kMaxBytes = (size_t)1 << 31;
+  if ((size_t)c->vocab_size * c->n_embd * esz >= kMaxBytes)
+    return bad("vocab_size * n_embd too large (the embedding matrix must be < 2 GiB)");
+  const size_t rows = (size_t)std::max(c->max_prefill_tokens, c->max_batch);
+  if (rows * 4 * c->n_embd * esz >= kMaxBytes)
+    return bad("max_prefill_tokens * 4 * n_embd too large (activations must be < 2 GiB)");
   return NGPT_OK;
 }
 

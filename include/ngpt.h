@@ -69,6 +69,9 @@ extern "C" {
  * 1 <= block_size <= 4096;
  * vocab_size >= 1; max_batch in [1, NGPT_MAX_BATCH];
  * max_prefill_tokens >= 1 bounds the sum of prompt lengths of one prefill.
+ * Every matrix stays below 2 GiB (the kernels use 32-bit buffer offsets):
+ * vocab_size * n_embd * sizeof(dtype) < 2^31 and
+ * max(max_prefill_tokens, max_batch) * 4 * n_embd * sizeof(dtype) < 2^31.
  */
 #define NGPT_MAX_BATCH 256
 typedef struct {

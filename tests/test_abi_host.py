@@ -68,6 +68,9 @@ def test_kv_bytes_known_values():
     (dict(n_layer=-1), ng.NGPT_E_CONFIG),
     (dict(bias=2), ng.NGPT_E_CONFIG),
     (dict(n_embd=96, n_head=3), ng.NGPT_E_CONFIG),  # bf16 needs n_embd % 64
+    # 32-bit buffer offsets: each matrix and activation buffer below 2 GiB
+    (dict(vocab_size=1 << 20, n_embd=1024, n_head=16), ng.NGPT_E_CONFIG),
+    (dict(max_prefill_tokens=1 << 20), ng.NGPT_E_CONFIG),
 ])
 def test_config_validation(change, code):
     w = synth.workload("gpt2_124m_b1")
