@@ -17,11 +17,13 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+// fp32 -> bf16, round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32
+// (checked bit-identical to integer round-to-nearest-even on every finite
+// fp32 input, denormals included).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <class T> __device__ __forceinline__ T from_f32(float x);
@@ -40,10 +42,15 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float* f) {
   }
 }
 
+// two values to bf16 (a in the low half), one instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) |
-         (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_hw_t{a, b}, bf16x2_hw_t));
 }
+
+// 2^x with the hardware v_exp_f32: the same value as exp2f wherever that is
+// a normal float, 2^-inf = 0; results below 2^-126 (softmax weights too
+// small to change any sum) come out as 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -70,8 +77,8 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* o,
                                             const float* o2, int n) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;
-  const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-  const float c = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
+  const float a = (m == -INFINITY) ? 0.f : exp2_fast(m - mn);
+  const float c = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
   l = l * a + l2 * c;
   for (int j = 0; j < n; ++j) o[j] = o[j] * a + o2[j] * c;
   m = mn;

@@ -181,13 +181,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     tmax = fmaxf(tmax, lane_xor16(tmax));
     tmax = fmaxf(tmax, lane_xor32(tmax));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = (s[t][i] == -INFINITY) ? 0.f : exp2f(s[t][i] - m_new);
+        const float p = (s[t][i] == -INFINITY) ? 0.f : exp2_fast(s[t][i] - m_new);
         s[t][i] = p;
         psum += p;
       }
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int o2 = 1; o2 < LPK; o2 <<= 1) s += __shfl_xor(s, o2, 64);
     if (u <= p) {
       const float mn = fmaxf(m, s);
-      const float a = exp2f(m - mn);  // m = -inf gives 0
-      const float pr = exp2f(s - mn);
+      const float a = exp2_fast(m - mn);  // m = -inf gives 0
+      const float pr = exp2_fast(s - mn);
       l = l * a + pr;
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = o[j] * a + pr * vf[pass][j];

@@ -677,7 +677,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
 #pragma unroll
             for (int ps = 0; ps < kPasses; ++ps) {
               const int u = key0 + ps * 8 + kgrp;
-              const float pr = (sc[ps] == -INFINITY) ? 0.f : exp2f(sc[ps] - mx);
+              const float pr = (sc[ps] == -INFINITY) ? 0.f : exp2_fast(sc[ps] - mx);
               lsum += pr;
               float vf[8];
               if (u == p) {
