@@ -34,9 +34,7 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
   } else {
     float v = acc;
     if (e.bias) v += to_f32(static_cast<const T*>(e.bias)[n]);
-    if constexpr (EPI == EPI_STORE) {
-      static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(v);
-    } else if constexpr (EPI == EPI_GELU) {
+    if constexpr (EPI == EPI_GELU) {
       static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(gelu_erf(v));
     } else if constexpr (EPI == EPI_RESID) {
       static_cast<float*>(e.out)[(size_t)r * e.ldo + n] += v;
@@ -96,7 +94,7 @@ __device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
 // (l % 16) of the first operand and column (l % 16) of the second, each as 8
 // consecutive K values starting at 8 * (l / 16); the 16x16 fp32 result holds
 // row 4 * (l / 16) + i, column l % 16 in element i of lane l.  For the bf16
-// outputs (q/k/v, GELU, plain store) the weight fragment goes first: each
+// outputs (q/k/v and GELU) the weight fragment goes first: each
 // 16x16 result is then a tile of (A W^T)^T, and lane l holds output row
 // (l % 16) at four consecutive columns, written with one 8-byte store.  For
 // the fp32 outputs (residual add, logits) the A fragment goes first, and 16
@@ -116,7 +114,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   constexpr int BCH = BN * 8 / 256;
   constexpr uint32_t kOut = 0x80000000u;  // offset past every buffer: reads 0
   // weight fragment first for the bf16-output epilogues (see the epilogue)
-  constexpr bool kSwap = (EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_STORE);
+  constexpr bool kSwap = (EPI == EPI_QKV || EPI == EPI_GELU);
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS];
 
@@ -281,7 +279,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         }
       }
     }
-  } else if constexpr (kSwap) {  // EPI_GELU, EPI_STORE: bf16 rows
+  } else if constexpr (kSwap) {  // EPI_GELU: bf16 rows
     const bool vec = (e.ldo & 3) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -291,8 +289,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         if (row >= M || col >= N) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         if (e.bias) v = add_bias4(static_cast<const bf16_t*>(e.bias), col, N, v);
-        if constexpr (EPI == EPI_GELU)
-          v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
+        v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
         bf16_t* o = static_cast<bf16_t*>(e.out) + (size_t)row * e.ldo + col;
         if (vec && col + 3 < N) {
           *reinterpret_cast<uint2*>(o) = pack_bf16x4(v);
@@ -822,11 +819,11 @@ void launch_linear(int dtype, int epi, const void* A, int lda,
                    const EpiArgs& e, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   switch (epi) {
-    case EPI_STORE: dispatch<EPI_STORE>(dtype, A, lda, ln, W, M, N, K, e, s); break;
     case EPI_GELU: dispatch<EPI_GELU>(dtype, A, lda, ln, W, M, N, K, e, s); break;
     case EPI_RESID: dispatch<EPI_RESID>(dtype, A, lda, ln, W, M, N, K, e, s); break;
     case EPI_QKV: dispatch<EPI_QKV>(dtype, A, lda, ln, W, M, N, K, e, s); break;
-    default: dispatch<EPI_LOGITS>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    case EPI_LOGITS: dispatch<EPI_LOGITS>(dtype, A, lda, ln, W, M, N, K, e, s); break;
+    default: break;   // (no other epilogue exists)
   }
 }
 

@@ -20,7 +20,6 @@ struct RowMap {
 
 // Linear-layer epilogues (what happens to acc = A W^T for row r, column n).
 enum Epi {
-  EPI_STORE = 0,   // out[r][n] = acc + bias                      (dtype)
   EPI_GELU = 1,    // out[r][n] = GELU(acc + bias)                (dtype)
   EPI_RESID = 2,   // out[r][n] += acc + bias                      (fp32 residual)
   EPI_QKV = 3,     // split into q (out, dtype) and the K/V cache rows
