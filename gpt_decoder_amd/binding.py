@@ -24,6 +24,7 @@ NGPT_E_SIZE = -4
 NGPT_E_CONTEXT = -5
 NGPT_E_HIP = -6
 NGPT_E_DEVICE = -7
+NGPT_E_TIMEOUT = -8
 NGPT_F32 = 0
 NGPT_BF16 = 1
 NGPT_MAX_BATCH = 256
@@ -92,6 +93,7 @@ def lib():
     L.ngpt_logits.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i32)]
     L.ngpt_copy_logits.argtypes = [vp, vp, i32, i32]
     L.ngpt_device_status.argtypes = [vp, ctypes.POINTER(i32)]
+    L.ngpt_set_wait_limit.argtypes = [vp, i32]
     L.ngpt_last_error.argtypes = [vp]
     L.ngpt_last_error.restype = ctypes.c_char_p
     L.ngpt_status_string.argtypes = [ctypes.c_int]
@@ -99,7 +101,7 @@ def lib():
     for name in ("ngpt_check_config", "ngpt_create", "ngpt_destroy",
                  "ngpt_set_sampling", "ngpt_prefill", "ngpt_decode_step",
                  "ngpt_decode_feed", "ngpt_sample", "ngpt_logits",
-                 "ngpt_copy_logits", "ngpt_device_status"):
+                 "ngpt_copy_logits", "ngpt_device_status", "ngpt_set_wait_limit"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -259,6 +261,10 @@ class Model:
         p, ld = ctypes.c_void_p(), ctypes.c_int32()
         self._check(lib().ngpt_logits(self.h, ctypes.byref(p), ctypes.byref(ld)))
         return p.value, ld.value
+
+    def set_wait_limit(self, passes: int = 0):
+        """Poll passes before a one-launch decode wait gives up (0: default)."""
+        self._check(lib().ngpt_set_wait_limit(self.h, int(passes)))
 
     def device_status(self) -> int:
         st = ctypes.c_int32()

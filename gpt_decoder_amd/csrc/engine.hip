@@ -56,6 +56,7 @@ struct GraphSlot {
   int32_t* lens = nullptr;
   int32_t* limit = nullptr;
   int32_t batch = 0;
+  int32_t wait_limit = 0;
   const void* arg_in = nullptr;   // uniforms (step) or feed ids (feed)
   int32_t* arg_out = nullptr;     // next_ids (step)
   SamplerArgs head_args;          // arguments of the head node
@@ -71,6 +72,7 @@ const char* status_name(int s) {
     case NGPT_E_CONTEXT: return "NGPT_E_CONTEXT";
     case NGPT_E_HIP: return "NGPT_E_HIP";
     case NGPT_E_DEVICE: return "NGPT_E_DEVICE";
+    case NGPT_E_TIMEOUT: return "NGPT_E_TIMEOUT";
     default: return "NGPT_E_UNKNOWN";
   }
 }
@@ -96,6 +98,7 @@ struct ngpt_model {
   float* part = nullptr;
   float* ppart = nullptr;   // prefill attention key-split partials (one sequence)
   int32_t *tok = nullptr, *pos = nullptr, *status = nullptr;
+  int32_t h_wait_limit = 0;        // one-launch decode poll limit (0: default)
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
   // one-launch batch-1 decode (see k_persist.hip)
@@ -331,6 +334,15 @@ int ngpt_destroy(ngpt_model* m) {
   return NGPT_OK;
 }
 
+int ngpt_set_wait_limit(ngpt_model* m, int32_t passes) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  // a kernel argument of the one-launch decode kernel (0: its default); a
+  // captured graph records the value it was captured with and is captured
+  // again when it changes
+  m->h_wait_limit = passes > 0 ? passes : 0;
+  return NGPT_OK;
+}
+
 int ngpt_set_sampling(ngpt_model* m, float temperature, int32_t top_k, int32_t greedy) {
   if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
   if (!greedy && !(temperature > 0.f))
@@ -453,7 +465,7 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   a.logits = m->logits;
   a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
   a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
-  a.epoch = m->epoch; a.status = m->status;
+  a.epoch = m->epoch; a.status = m->status; a.wait_limit = m->h_wait_limit;
   return a;
 }
 
@@ -550,6 +562,7 @@ static int capture(ngpt_model* m, GraphSlot& g, const ngpt_kv* kv, int mode,
   g.graph = graph; g.exec = exec; g.head = root;
   g.k = kv->k; g.v = kv->v; g.lens = kv->lens; g.limit = kv->limit;
   g.batch = kv->batch; g.arg_in = arg_in; g.arg_out = arg_out;
+  g.wait_limit = m->h_wait_limit;
   g.head_args = a;
   return NGPT_OK;
 }
@@ -577,7 +590,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   }
   const bool same_kv = g.exec && g.k == kv->k && g.v == kv->v &&
                        g.lens == kv->lens && g.limit == kv->limit &&
-                       g.batch == kv->batch;
+                       g.batch == kv->batch && g.wait_limit == m->h_wait_limit;
   if (!same_kv) {
     rc = capture(m, g, kv, mode, arg_in, arg_out);
     if (rc != NGPT_OK) return rc;
@@ -660,7 +673,8 @@ int ngpt_device_status(ngpt_model* m, int32_t* status) {
   clear_status_kernel<<<1, 64, 0, m->stream>>>(m->status);
   HIP_TRY(m, hipGetLastError());
   HIP_TRY(m, hipStreamSynchronize(m->stream));
-  *status = v ? NGPT_E_DEVICE : NGPT_OK;
+  // bit 2: a one-launch decode wait gave up; bit 1: an id out of range
+  *status = (v & 2) ? NGPT_E_TIMEOUT : v ? NGPT_E_DEVICE : NGPT_OK;
   return NGPT_OK;
 }
 

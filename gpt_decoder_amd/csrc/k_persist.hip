@@ -53,7 +53,13 @@ constexpr int kCompute = 4;                 // compute wavefronts
 constexpr int kNSync = 2;                   // sync wavefronts (after the compute ones)
 constexpr int kThreads = 64 * (kCompute + kNSync);
 constexpr int kSyncLanes = 64 * kNSync;
-constexpr int kSpinLimit = 1 << 20;
+constexpr int kSpinLimit = 1 << 20;         // default poll passes per wait
+
+// Where a wait reports a timeout (status bit 2) and after how many passes.
+struct WaitCtl {
+  int32_t* status;
+  int limit;
+};
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr int kHs = 64;          // head size
 constexpr int kChunk = 32;       // keys per attention chunk (one wavefront)
@@ -111,11 +117,11 @@ __device__ __forceinline__ void put_word(float* dst, int k, uint64_t v) {
 // every word that carries ep (a word does not change once tagged, so copying
 // it again is harmless); the wait ends on the first pass with nothing
 // missing.  No per-word bookkeeping is carried between passes.  False after
-// kSpinLimit passes (status bit 2).
+// wc.limit passes (status bit 2).
 template <int NJ, bool PACK>
 __device__ __forceinline__ bool sync_wave_wait(const uint64_t* src, int n,
                                                uint32_t ep, float* dst,
-                                               int32_t* status) {
+                                               WaitCtl wc) {
   const int sl = static_cast<int>(threadIdx.x) - 64 * kCompute;
   for (int spin = 0;; ++spin) {
     uint64_t v[NJ];
@@ -130,8 +136,8 @@ __device__ __forceinline__ bool sync_wave_wait(const uint64_t* src, int n,
       miss |= in && !got;
     }
     if (!__any(miss)) return true;
-    if (spin >= kSpinLimit) {
-      if ((sl & 63) == 0) atomicOr(status, 2);
+    if (spin >= wc.limit) {
+      if ((sl & 63) == 0) atomicOr(wc.status, 2);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -142,7 +148,7 @@ __device__ __forceinline__ bool sync_wave_wait(const uint64_t* src, int n,
 // v (at e + ko, e + vo), into sq[0:64), sq[64:128), sq[128:192).
 __device__ __forceinline__ bool sync_wave_wait_qkv(const uint64_t* e, int qo, int ko,
                                                    int vo, bool kv, uint32_t ep,
-                                                   float* sq, int32_t* status) {
+                                                   float* sq, WaitCtl wc) {
   const int lane = threadIdx.x & 63, hl = lane & 31;
   const bool lo = lane < 32;
   const uint64_t* a0 = e + (lo ? qo : ko) + hl;
@@ -157,8 +163,8 @@ __device__ __forceinline__ bool sync_wave_wait_qkv(const uint64_t* e, int qo, in
     if (in0 && g0) put_word<true>(d0, hl, v0);
     if (in1 && g1) put_word<true>(sq + 2 * kHs, hl, v1);
     if (!__any((in0 && !g0) || (in1 && !g1))) return true;
-    if (spin >= kSpinLimit) {
-      if (lane == 0) atomicOr(status, 2);
+    if (spin >= wc.limit) {
+      if (lane == 0) atomicOr(wc.status, 2);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -178,23 +184,23 @@ static_assert(kSyncLanes == 128, "the load counts below assume two sync wavefron
 template <int KIND>
 __device__ __forceinline__ bool sync_wave_wait_n(const uint64_t* src, int n,
                                                  uint32_t ep, float* dst,
-                                                 int32_t* status) {
+                                                 WaitCtl wc) {
   if constexpr (KIND == kWaitRec) {
-    if (n <= 128) return sync_wave_wait<1, false>(src, n, ep, dst, status);
-    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, status);
-    return sync_wave_wait<4, false>(src, n, ep, dst, status);
+    if (n <= 128) return sync_wave_wait<1, false>(src, n, ep, dst, wc);
+    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, wc);
+    return sync_wave_wait<4, false>(src, n, ep, dst, wc);
   } else if constexpr (KIND == kWaitY) {
-    if (n <= 128) return sync_wave_wait<1, true>(src, n, ep, dst, status);
-    if (n <= 256) return sync_wave_wait<2, true>(src, n, ep, dst, status);
-    return sync_wave_wait<3, true>(src, n, ep, dst, status);
+    if (n <= 128) return sync_wave_wait<1, true>(src, n, ep, dst, wc);
+    if (n <= 256) return sync_wave_wait<2, true>(src, n, ep, dst, wc);
+    return sync_wave_wait<3, true>(src, n, ep, dst, wc);
   } else if constexpr (KIND == kWaitC) {
-    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, status);
-    if (n <= 512) return sync_wave_wait<4, false>(src, n, ep, dst, status);
-    return sync_wave_wait<6, false>(src, n, ep, dst, status);
+    if (n <= 256) return sync_wave_wait<2, false>(src, n, ep, dst, wc);
+    if (n <= 512) return sync_wave_wait<4, false>(src, n, ep, dst, wc);
+    return sync_wave_wait<6, false>(src, n, ep, dst, wc);
   } else {
-    if (n <= 512) return sync_wave_wait<4, true>(src, n, ep, dst, status);
-    if (n <= 1024) return sync_wave_wait<8, true>(src, n, ep, dst, status);
-    return sync_wave_wait<12, true>(src, n, ep, dst, status);
+    if (n <= 512) return sync_wave_wait<4, true>(src, n, ep, dst, wc);
+    if (n <= 1024) return sync_wave_wait<8, true>(src, n, ep, dst, wc);
+    return sync_wave_wait<12, true>(src, n, ep, dst, wc);
   }
 }
 
@@ -473,11 +479,13 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
 
   const bool sync0 = SYNC && __builtin_amdgcn_readfirstlane(wave) == kCompute;  // first sync wavefront
   int seq = 0;
+  // every wait gives up after the host-set number of passes (0: the default)
+  const WaitCtl wc{a.status, a.wait_limit > 0 ? a.wait_limit : kSpinLimit};
   // n == 0: nothing to poll, the wait is just the barrier
   auto wait_in = [&](auto kind, const uint64_t* src, int n, float* dst) -> bool {
     ++seq;
     if constexpr (SYNC) {
-      if (n > 0 && !sync_wave_wait_n<decltype(kind)::value>(src, n, ep, dst, a.status) &&
+      if (n > 0 && !sync_wave_wait_n<decltype(kind)::value>(src, n, ep, dst, wc) &&
           lane == 0)
         S.fail = seq;
     }
@@ -558,8 +566,8 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
     // the sync wavefronts pick it and write x = wte[tok] + wpe[p].
     ++seq;
     if constexpr (SYNC) {
-      if (!sync_wave_wait<(2 * kMaxGrid) / kSyncLanes, false>(a.e_cand, 2 * G, ep - 1u, bCand,
-                                                                a.status) && lane == 0)
+      if (!sync_wave_wait<(2 * kMaxGrid) / kSyncLanes, false>(a.e_cand, 2 * G, ep - 1u, bCand, wc) &&
+          lane == 0)
         S.fail = seq;
     }
     __syncthreads();
@@ -633,7 +641,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
       ++seq;   // wait: q of head h (with the new k, v for the last item)
       if (sync0) {
         if (!sync_wave_wait_qkv(e_qkv, h * kHs / 2, (C + h * kHs) / 2, (2 * C + h * kHs) / 2,
-                                last, ep, sq, a.status) && lane == 0)
+                                last, ep, sq, wc) && lane == 0)
           S.fail = seq;
       }
       __syncthreads();

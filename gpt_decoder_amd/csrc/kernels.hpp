@@ -170,7 +170,8 @@ struct PersistArgs {
   // exchange words (fp32 value | epoch << 32), per layer
   uint64_t *e_qkv, *e_rec, *e_y, *e_x1, *e_f, *e_x2;
   uint32_t* epoch;              // advanced once per launch
-  int32_t* status;              // bit 1: a wait timed out
+  int32_t* status;              // bit 2: a wait timed out
+  int wait_limit;                // poll passes before a wait gives up (0: default)
 };
 
 bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,

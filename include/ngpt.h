@@ -56,6 +56,7 @@ extern "C" {
 #define NGPT_E_CONTEXT   -5  /* no sequence can take another token          */
 #define NGPT_E_HIP       -6  /* a HIP runtime call failed                   */
 #define NGPT_E_DEVICE    -7  /* a kernel reported an out-of-range id        */
+#define NGPT_E_TIMEOUT   -8  /* a wait in the one-launch decode kernel gave up */
 
 /* Element types. */
 #define NGPT_F32   0
@@ -237,10 +238,25 @@ int ngpt_copy_logits(ngpt_model *m, float *dst, int32_t ld_dst, int32_t B);
 
 /*
  * Synchronise the stream and report kernel-side input errors since the last
- * call: *status = NGPT_OK or NGPT_E_DEVICE (an id outside [0, vocab) was
- * seen).  Clears the flag.
+ * call: *status = NGPT_OK, NGPT_E_DEVICE (an id outside [0, vocab) was
+ * seen) or NGPT_E_TIMEOUT (a wait inside the one-launch decode kernel gave
+ * up, see ngpt_set_wait_limit: that step's ids, logits and cache rows are
+ * invalid, and the sequence must be prefilled again).  A timeout is reported
+ * ahead of an id error.  Clears the flags.
  */
 int ngpt_device_status(ngpt_model *m, int32_t *status);
+
+/*
+ * Poll passes after which a wait inside the one-launch decode kernel (batch
+ * 1, bf16) gives up and sets the timeout flag; passes <= 0 restores the
+ * default, 2^20 passes (tens of milliseconds).  Every wait in that kernel is
+ * bounded this way, so a launch whose partners never answer ends instead of
+ * hanging.  A small limit is a test hook that makes the timeout path run
+ * (1: give up after the second pass that finds a word missing).  Takes
+ * effect for later calls (a captured decode graph is captured again).
+ * Errors: NGPT_E_ARG.
+ */
+int ngpt_set_wait_limit(ngpt_model *m, int32_t passes);
 
 /* Message of the last error on this handle (static storage if m is NULL). */
 const char *ngpt_last_error(const ngpt_model *m);

@@ -142,3 +142,5 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.ngpt_decode_feed(None, None, None) == ng.NGPT_E_ARG
     assert lib.ngpt_sample(None, None, 1, 1, None, None) == ng.NGPT_E_ARG
     assert lib.ngpt_status_string(-5) == b"NGPT_E_CONTEXT"
+    assert lib.ngpt_status_string(ng.NGPT_E_TIMEOUT) == b"NGPT_E_TIMEOUT"
+    assert lib.ngpt_set_wait_limit(None, 1) == ng.NGPT_E_ARG

@@ -354,3 +354,43 @@ def test_fp32_rows_wider_than_the_streaming_kernel(B):
     log(f"  fp32 C=1280 B={B}: max logit err {worst:.2e}")
     assert worst < TOL_F32
     m.close()
+
+
+@pytest.mark.gpu
+def test_one_launch_decode_wait_timeout_is_reported_and_recovered():
+    """Every wait of the one-launch decode kernel is bounded.  With the limit
+    set to one pass the waits give up: the launches still end, the timeout
+    is reported (ahead of the id error the timed-out greedy pick raises), and
+    once the limit is restored and the prompt prefilled again, decoding
+    matches the oracle."""
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    V = 500
+    w = synth.Workload("timeout_2_4_256", 13, 2, 4, 256, 64, V, V, False, "bf16",
+                       batch=1, prompt_len=8)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(99).integers(0, V, (1, 8)).astype(np.int32)
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(1)
+    gpu_prefill(m, kv, ids, [8])
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    m.set_wait_limit(1)
+    m.decode_step(kv, nxt, None)   # graph: sampler node + one-launch forward
+    m.decode_step(kv, nxt, None)   # one launch with the greedy pick folded in
+    assert m.device_status() == ng.NGPT_E_TIMEOUT
+    assert m.device_status() == 0  # the flags were cleared
+    m.set_wait_limit(0)
+    o = oracle.OracleGPT(w, W, act_bf16=True)
+    worst = max_abs(gpu_prefill(m, kv, ids, [8]), o.prefill(ids, [8]))
+    prev = m.logits(1).cpu().numpy()
+    for _ in range(6):
+        m.decode_step(kv, nxt, None)
+        tok = int(nxt.cpu().numpy()[0])
+        assert tok == int(np.argmax(prev[0]))
+        prev = m.logits(1).cpu().numpy()
+        worst = max(worst, max_abs(prev, o.decode([tok])))
+    assert m.device_status() == 0
+    log(f"  after the timeout: max logit err {worst:.2e}")
+    assert worst < TOL_BF16
+    m.close()
