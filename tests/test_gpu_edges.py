@@ -281,13 +281,14 @@ def test_fused_greedy_step_matches_sampler_head_node():
         assert g_ids[s] == int(np.argmax(g_lg[s - 1]))
 
 
-@pytest.mark.parametrize("L,H,C,Tb,plen,steps", [
-    (2, 1, 64, 512, 300, 6),     # one head; three attention items per head
-    (1, 8, 512, 1024, 1000, 6),  # eight items per head near the block end
-    (3, 12, 768, 1024, 1015, 8),  # GPT-2 width, positions up to 1022
-    (2, 4, 256, 64, 10, 40),     # short block, decoded up to its limit
+@pytest.mark.parametrize("L,H,C,Tb,plen,steps,bias", [
+    (2, 1, 64, 512, 300, 6, False),     # one head; three attention items per head
+    (1, 8, 512, 1024, 1000, 6, False),  # eight items per head near the block end
+    (3, 12, 768, 1024, 1015, 8, False),  # GPT-2 width, positions up to 1022
+    (2, 4, 256, 64, 10, 40, False),     # short block, decoded up to its limit
+    (2, 12, 768, 256, 140, 12, True),   # GPT-2 width with LayerNorm and Linear biases
 ])
-def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps):
+def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps, bias):
     """Batch-1 bf16 decode with hs 64 runs as one launch per token.  Its
     work split depends on the shape and the position (row pairs per
     workgroup, attention items per head and their XCD placement, record
@@ -296,7 +297,7 @@ def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps):
     are checked against the oracle's KV-cached decode of the same ids."""
     torch = need_gpu()
     V = 500
-    w = synth.Workload(f"persist_{L}_{H}_{C}_{Tb}", 11, L, H, C, Tb, V, V, False,
+    w = synth.Workload(f"persist_{L}_{H}_{C}_{Tb}_{int(bias)}", 11, L, H, C, Tb, V, V, bias,
                        "bf16", batch=1, prompt_len=plen)
     W = synth.make_weights(w, gamma_std=0.1)
     rng = np.random.default_rng(C + Tb)
@@ -321,7 +322,7 @@ def test_one_launch_decode_shapes_against_oracle(L, H, C, Tb, plen, steps):
         worst = max(worst, max_abs(prev, o.decode([tok])))
     assert m.device_status() == 0
     assert int(kv.lens.cpu().numpy()[0]) == plen + min(steps, Tb - plen)
-    log(f"  L={L} H={H} C={C} Tb={Tb} p0={plen}: max logit err {worst:.2e}")
+    log(f"  L={L} H={H} C={C} Tb={Tb} p0={plen} bias={bias}: max logit err {worst:.2e}")
     assert worst < TOL_BF16
     m.close()
 
