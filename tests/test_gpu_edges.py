@@ -8,8 +8,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (TOL_BF16, TOL_F32, dev_f64, dev_i32, gpu_prefill, log,
-                        make_model, make_oracle, max_abs, need_gpu, tol_for)
+from gpu_common import (TOL_BF16, TOL_F32, dev_f64, dev_i32, draws_must_agree, gpu_prefill,
+                        log, make_model, make_oracle, max_abs, need_gpu, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -393,5 +393,48 @@ def test_one_launch_decode_wait_timeout_is_reported_and_recovered():
         worst = max(worst, max_abs(prev, o.decode([tok])))
     assert m.device_status() == 0
     log(f"  after the timeout: max logit err {worst:.2e}")
+    assert worst < TOL_BF16
+    m.close()
+
+
+@pytest.mark.gpu
+def test_one_launch_decode_sampled_batch1():
+    """Batch-1 sampled decode (temperature 0.9, top-k 40) runs the sampler
+    node and the one-launch forward as one captured graph.  Every drawn id
+    equals the sampler's own pick on the same logits and uniform
+    (bit-exact), draws that the oracle's logits decide beyond doubt agree
+    with the oracle, and the new logits match the oracle's decode of the
+    drawn id."""
+    torch = need_gpu()
+    V, T, K, n = 500, 0.9, 40, 30
+    w = synth.Workload("sampled_b1_2l768", 17, 2, 12, 768, 128, V, V, False, "bf16",
+                       batch=1, prompt_len=20)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(5).integers(0, V, (1, 20)).astype(np.int32)
+    uni = np.random.default_rng(6).random((n, 1))
+    m = make_model(w, W)
+    m.set_sampling(temperature=T, top_k=K)
+    kv = m.new_kv(1)
+    o = oracle.OracleGPT(w, W, act_bf16=True)
+    ref_lg = o.prefill(ids, [20])
+    got_lg = gpu_prefill(m, kv, ids, [20])
+    worst = max_abs(got_lg, ref_lg)
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    need_n = 0
+    for s in range(n):
+        u = dev_f64(uni[s])
+        want = m.sample(torch.from_numpy(got_lg.astype(np.float32)).cuda(), u).cpu().numpy()
+        ref_ids, _, marg = oracle.sample_rows(ref_lg.astype(np.float32), uni[s], T, K, False)
+        need = draws_must_agree(ref_lg, got_lg, marg, T, K)
+        m.decode_step(kv, nxt, u)
+        tok = nxt.cpu().numpy()
+        assert np.array_equal(tok, want), f"step {s}: graph draw differs from the sampler's"
+        assert np.array_equal(tok[need], ref_ids[need]), f"step {s}: draw differs from the oracle's"
+        need_n += int(need.sum())
+        ref_lg = o.decode([int(tok[0])])
+        got_lg = m.logits(1).cpu().numpy()
+        worst = max(worst, max_abs(got_lg, ref_lg))
+    assert m.device_status() == 0
+    log(f"  batch-1 sampled: max logit err {worst:.2e}; draws beyond doubt {need_n}/{n}")
     assert worst < TOL_BF16
     m.close()
