@@ -438,3 +438,25 @@ def test_one_launch_decode_sampled_batch1():
     log(f"  batch-1 sampled: max logit err {worst:.2e}; draws beyond doubt {need_n}/{n}")
     assert worst < TOL_BF16
     m.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("H,C", [(8, 256), (4, 256)])
+def test_prefill_key_split_head_sizes(H, C):
+    """A long batch-1 prompt splits the keys of its later query tiles into
+    chunks whose (max, sum, output) records a second kernel merges in chunk
+    order; both head sizes (32 and 64) against the oracle's prefill."""
+    need_gpu()
+    V = 300
+    w = synth.Workload(f"split_{H}_{C}", 19, 2, H, C, 512, V, V, False, "bf16",
+                       batch=1, prompt_len=450)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(H).integers(0, V, (1, 450)).astype(np.int32)
+    m = make_model(w, W)
+    kv = m.new_kv(1)
+    o = oracle.OracleGPT(w, W, act_bf16=True)
+    err = max_abs(gpu_prefill(m, kv, ids, [450]), o.prefill(ids, [450]))
+    assert m.device_status() == 0
+    log(f"  hs={C // H}: 450-token prefill, max logit err {err:.2e}")
+    assert err < TOL_BF16
+    m.close()
