@@ -460,3 +460,40 @@ def test_prefill_key_split_head_sizes(H, C):
     log(f"  hs={C // H}: 450-token prefill, max logit err {err:.2e}")
     assert err < TOL_BF16
     m.close()
+
+
+@pytest.mark.gpu
+def test_one_launch_decode_stops_at_the_sequence_limit():
+    """Batch 1 through the one-launch kernel (the first step behind the
+    sampler node, then fused greedy steps): a prefill limit of prompt + 3
+    allows exactly three steps, the fourth returns NGPT_E_CONTEXT, and the
+    tokens and logits of the three match the oracle."""
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    V = 400
+    w = synth.Workload("limit_b1_2l256", 23, 2, 4, 256, 64, V, V, False, "bf16",
+                       batch=1, prompt_len=12)
+    W = synth.make_weights(w)
+    ids = np.random.default_rng(23).integers(0, V, (1, 12)).astype(np.int32)
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(1)
+    o = oracle.OracleGPT(w, W, act_bf16=True)
+    m.prefill(kv, dev_i32(ids), [12], [15])
+    ref = o.prefill(ids, [12])
+    worst = max_abs(m.logits(1).cpu().numpy(), ref)
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        m.decode_step(kv, nxt, None)
+        tok = int(nxt.cpu().numpy()[0])
+        assert tok == int(np.argmax(ref[0]))
+        ref = o.decode([tok])
+        worst = max(worst, max_abs(m.logits(1).cpu().numpy(), ref))
+    assert kv.lens.cpu().tolist() == [15]
+    with pytest.raises(ng.NgptError) as ei:
+        m.decode_step(kv, nxt, None)
+    assert ei.value.code == ng.NGPT_E_CONTEXT
+    assert kv.lens.cpu().tolist() == [15]
+    assert m.device_status() == 0
+    assert worst < TOL_BF16
+    m.close()
