@@ -29,7 +29,7 @@ DECODE_KERNEL = "decode_persistent_kernel"
 # the decode kernel's sources and the file that picks its launch grid: the
 # counter summary is valid only for exactly these
 KERNEL_SOURCES = [os.path.join(ROOT, "gpt_decoder_amd", "csrc", f)
-                  for f in ("k_persist.hip", "common.hpp", "kernels.hpp", "engine.hip")]
+                  for f in ("k_persist.hip", "k_persist.hpp", "common.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_persistent_gpt2_124m_b1_traffic.txt")
 
 

@@ -4,7 +4,7 @@ The compute lives in ``libngpt.so`` (hand-written HIP kernels for gfx950,
 C ABI in ``include/ngpt.h``); this package is its ctypes binding plus the
 in-tree build script.
 """
-from .binding import (Config, KVCache, Model, NgptError, check_config,
+from .binding import (workspace_bytes, Config, KVCache, Model, NgptError, check_config,
                       kv_bytes, lib, make_config, model_from_workload,
                       LIB_PATH, NGPT_OK, NGPT_E_ARG, NGPT_E_CONFIG,
                       NGPT_E_RANGE, NGPT_E_SIZE, NGPT_E_CONTEXT, NGPT_E_HIP,

@@ -79,27 +79,33 @@ def lib():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.ngpt_kv_bytes.argtypes = [ctypes.POINTER(Config), i32]
     L.ngpt_kv_bytes.restype = sz
+    L.ngpt_workspace_bytes.argtypes = [ctypes.POINTER(Config)]
+    L.ngpt_workspace_bytes.restype = sz
     L.ngpt_check_config.argtypes = [ctypes.POINTER(Config)]
     L.ngpt_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
-                              vp, ctypes.POINTER(vp)]
+                              vp, sz, vp, ctypes.POINTER(vp)]
     L.ngpt_destroy.argtypes = [vp]
     L.ngpt_set_sampling.argtypes = [vp, ctypes.c_float, i32, i32]
     L.ngpt_prefill.argtypes = [vp, ctypes.POINTER(KV), vp,
                                ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
                                i32]
+    L.ngpt_prefill_device.argtypes = [vp, ctypes.POINTER(KV), vp,
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                      i32, i32]
     L.ngpt_decode_step.argtypes = [vp, ctypes.POINTER(KV), vp, vp]
     L.ngpt_decode_feed.argtypes = [vp, ctypes.POINTER(KV), vp]
     L.ngpt_sample.argtypes = [vp, vp, i32, i32, vp, vp]
     L.ngpt_logits.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i32)]
     L.ngpt_copy_logits.argtypes = [vp, vp, i32, i32]
-    L.ngpt_device_status.argtypes = [vp, ctypes.POINTER(i32)]
+    L.ngpt_device_status.argtypes = [vp, vp]
     L.ngpt_set_wait_limit.argtypes = [vp, i32]
     L.ngpt_last_error.argtypes = [vp]
     L.ngpt_last_error.restype = ctypes.c_char_p
     L.ngpt_status_string.argtypes = [ctypes.c_int]
     L.ngpt_status_string.restype = ctypes.c_char_p
     for name in ("ngpt_check_config", "ngpt_create", "ngpt_destroy",
-                 "ngpt_set_sampling", "ngpt_prefill", "ngpt_decode_step",
+                 "ngpt_set_sampling", "ngpt_prefill", "ngpt_prefill_device",
+                 "ngpt_decode_step",
                  "ngpt_decode_feed", "ngpt_sample", "ngpt_logits",
                  "ngpt_copy_logits", "ngpt_device_status", "ngpt_set_wait_limit"):
         getattr(L, name).restype = ctypes.c_int
@@ -123,6 +129,10 @@ def make_config(n_layer, n_head, n_embd, block_size, vocab_size, bias, dtype,
 
 def kv_bytes(cfg: Config, batch: int) -> int:
     return int(lib().ngpt_kv_bytes(ctypes.byref(cfg), batch))
+
+
+def workspace_bytes(cfg: Config) -> int:
+    return int(lib().ngpt_workspace_bytes(ctypes.byref(cfg)))
 
 
 def check_config(cfg: Config) -> int:
@@ -192,9 +202,16 @@ class Model:
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         self.stream = stream
+        # caller-owned workspace (torch's allocations are 256-byte aligned)
+        nws = workspace_bytes(self.cfg)
+        if nws == 0:
+            raise NgptError(NGPT_E_CONFIG, "invalid config")
+        self.workspace = torch.empty(nws, dtype=torch.uint8, device=self.device)
+        self._status = torch.zeros(1, dtype=torch.int32, device=self.device)
         h = ctypes.c_void_p()
         rc = lib().ngpt_create(ctypes.byref(self.cfg),
                                ctypes.byref(self._weights),
+                               _ptr(self.workspace), nws,
                                ctypes.c_void_p(stream.cuda_stream),
                                ctypes.byref(h))
         if rc != NGPT_OK:
@@ -216,14 +233,22 @@ class Model:
 
     def prefill(self, kv: KVCache, ids, lens: Sequence[int],
                 limit: Optional[Sequence[int]] = None):
-        """``ids``: device int32 [B, Tmax]; ``lens``/``limit``: host ints."""
+        """``ids``: int32 [B, Tmax], host (numpy; checked by the library) or
+        device (torch, ngpt_prefill_device); ``lens``/``limit``: host ints."""
         B, Tmax = ids.shape
-        assert ids.dtype == self.torch.int32 and ids.is_contiguous()
         lens_a = (ctypes.c_int32 * B)(*[int(x) for x in lens])
         lim_a = None if limit is None else (ctypes.c_int32 * B)(
             *[int(x) for x in limit])
-        self._check(lib().ngpt_prefill(self.h, ctypes.byref(kv.struct),
-                                       _ptr(ids), lens_a, lim_a, B, Tmax))
+        if self.torch.is_tensor(ids) and ids.is_cuda:
+            assert ids.dtype == self.torch.int32 and ids.is_contiguous()
+            self._check(lib().ngpt_prefill_device(
+                self.h, ctypes.byref(kv.struct), _ptr(ids), lens_a, lim_a, B,
+                Tmax))
+            return
+        a = np.ascontiguousarray(np.asarray(ids), dtype=np.int32)
+        self._check(lib().ngpt_prefill(
+            self.h, ctypes.byref(kv.struct),
+            a.ctypes.data_as(ctypes.c_void_p), lens_a, lim_a, B, Tmax))
 
     def decode_step(self, kv: KVCache, next_ids, uniforms):
         """``next_ids``: device int32 [batch] (out); ``uniforms``: device
@@ -267,9 +292,10 @@ class Model:
         self._check(lib().ngpt_set_wait_limit(self.h, int(passes)))
 
     def device_status(self) -> int:
-        st = ctypes.c_int32()
-        self._check(lib().ngpt_device_status(self.h, ctypes.byref(st)))
-        return st.value
+        """Kernel-side status since the last call (the library enqueues the
+        read; this waits for it)."""
+        self._check(lib().ngpt_device_status(self.h, _ptr(self._status)))
+        return int(self._status.item())
 
     def close(self):
         if getattr(self, "h", None):

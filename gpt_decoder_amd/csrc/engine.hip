@@ -39,8 +39,41 @@ __global__ void set_lens_kernel(LensArgs a, int32_t* lens, int32_t* limit) {
   }
 }
 
-__global__ void clear_status_kernel(int32_t* status) {
-  if (threadIdx.x == 0) status[0] = 0;
+// Report and clear the kernel-side flags: bit 2 a one-launch decode wait
+// gave up, bit 1 invalid input (an id out of range, or a greedy row with no
+// finite maximum).  `out` is device memory or device-writable host memory.
+__global__ void read_status_kernel(int32_t* status, int32_t* out) {
+  if (threadIdx.x == 0) {
+    const int32_t v = status[0];
+    out[0] = (v & 2) ? NGPT_E_TIMEOUT : v ? NGPT_E_DEVICE : NGPT_OK;
+    status[0] = 0;
+  }
+}
+
+// Sampling parameters written on the stream from a kernel argument, so that
+// setting them needs no host copy and no wait.
+__global__ void set_params_kernel(SampleParams* dst, SampleParams p) {
+  if (threadIdx.x == 0) *dst = p;
+}
+
+// Zero the workspace (a fill kernel rather than a memset node, so the same
+// code is safe to record in a graph).
+__global__ void zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The one-launch decode kernel's table of block weight pointers, written
+// from kernel arguments in chunks (no host staging to keep alive).
+constexpr int kTableChunk = 16;
+struct LayerTableChunk {
+  int32_t first, n;
+  PersistLayer l[kTableChunk];
+};
+__global__ void set_layer_table_kernel(PersistLayer* dst, LayerTableChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.n) dst[c.first + i] = c.l[i];
 }
 
 constexpr size_t kAlign = 256;
@@ -81,6 +114,16 @@ std::string g_static_error;
 
 }  // namespace
 
+// Byte offsets of the workspace regions (every region 256-byte aligned).
+struct WsLayout {
+  size_t x, h, q, y, f, z, logits, row_b, row_pos, last_rows, part, ppart, ids,
+      tok, pos, status, params, done;
+  // one-launch decode exchange buffers (absent: persist_shape == false)
+  bool persist_shape = false;
+  size_t eq, er, ey, e1, ef, e2, epoch, ecand, dlayers;
+  size_t total = 0;
+};
+
 struct ngpt_model {
   ngpt_config cfg{};
   int L = 0, H = 0, C = 0, hs = 0, Tb = 0, V = 0, Mmax = 0, nchunk = 0;
@@ -88,19 +131,27 @@ struct ngpt_model {
   const void *wte = nullptr, *wpe = nullptr, *lnf_w = nullptr, *lnf_b = nullptr;
   std::vector<ngpt_layer_weights> layers;
   hipStream_t stream = nullptr;
-  hipStream_t cap = nullptr;
-  // workspace
+  hipStream_t cap = nullptr;       // graph capture stream (created on first use)
+  // workspace (caller-owned)
   void* ws = nullptr;
+  size_t ws_bytes = 0;
   float* x = nullptr;
   void *h = nullptr, *q = nullptr, *y = nullptr, *f = nullptr, *z = nullptr;
   float* logits = nullptr;
   int32_t *row_b = nullptr, *row_pos = nullptr, *last_rows = nullptr;
   float* part = nullptr;
   float* ppart = nullptr;   // prefill attention key-split partials (one sequence)
+  int32_t* d_ids = nullptr; // packed prompt ids copied from the host
   int32_t *tok = nullptr, *pos = nullptr, *status = nullptr;
   int32_t h_wait_limit = 0;        // one-launch decode poll limit (0: default)
   SampleParams* params = nullptr;
   SampleParams h_params{1.0f, 0, 1, 0};  // host copy of *params
+  // pinned staging of host prompt ids: two halves, each reused only after
+  // the copy that last read it has completed (created on first use)
+  int32_t* pinned = nullptr;
+  hipEvent_t pinned_ev[2] = {nullptr, nullptr};
+  bool pinned_used[2] = {false, false};
+  int pinned_half = 0;
   // one-launch batch-1 decode (see k_persist.hip)
   int persist_grid = 0;   // workgroups of the one-launch decode kernel
   bool persist = false;
@@ -108,9 +159,11 @@ struct ngpt_model {
   uint64_t *e_qkv = nullptr, *e_rec = nullptr, *e_y = nullptr, *e_x1 = nullptr,
            *e_f = nullptr, *e_x2 = nullptr;
   uint32_t* epoch = nullptr;
+  uint32_t* done = nullptr;     // departure counter of the one-launch kernel
   uint64_t* e_cand = nullptr;   // greedy candidates left by the last launch
   bool cand_ok = false;         // the current logits came from that launch
-  // host record of the KV batch state
+  // the KV cache of the last prefill and the host record of its lengths
+  ngpt_kv rec_kv{};
   std::vector<int32_t> h_lens, h_limit;
   GraphSlot g_step, g_feed;
   std::string err;
@@ -183,13 +236,49 @@ size_t ngpt_kv_bytes(const ngpt_config* cfg, int32_t batch) {
          (cfg->n_embd / cfg->n_head) * es;
 }
 
-int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
-                ngpt_model** out) {
-  if (!out) return fail(nullptr, NGPT_E_ARG, "out is NULL");
-  *out = nullptr;
-  std::string why;
-  int rc = check_config(cfg, &why);
-  if (rc != NGPT_OK) return fail(nullptr, rc, why);
+}  // extern "C"
+
+// The workspace regions of a config.  Host-only: the one-launch decode
+// buffers are sized for the largest grid the kernel supports, so the layout
+// does not depend on the device.
+static WsLayout ws_layout(const ngpt_config* cfg) {
+  WsLayout o;
+  const size_t Mm = std::max(cfg->max_prefill_tokens, cfg->max_batch);
+  const size_t Bm = cfg->max_batch, C = cfg->n_embd;
+  const size_t es = cfg->dtype == NGPT_BF16 ? 2 : 4;
+  const int H = cfg->n_head, hs = cfg->n_embd / cfg->n_head, Tb = cfg->block_size;
+  const int nchunk = attn_decode_chunks(Tb);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { size_t r = off; off += align_up(bytes); return r; };
+  o.x = carve(Mm * C * 4); o.h = carve(Mm * C * es); o.q = carve(Mm * C * es);
+  o.y = carve(Mm * C * es); o.f = carve(Mm * 4 * C * es); o.z = carve(Bm * C * es);
+  o.logits = carve(Bm * (size_t)cfg->vocab_size * 4);
+  o.row_b = carve(Mm * 4); o.row_pos = carve(Mm * 4); o.last_rows = carve(Bm * 4);
+  o.part = carve(Bm * H * (size_t)nchunk * (hs + 2) * 4);
+  o.ppart = carve((size_t)H * Tb * attn_prefill_split_chunks(Tb) * (hs + 4) * 4);
+  o.ids = carve((size_t)cfg->max_prefill_tokens * 4);
+  o.tok = carve(Bm * 4); o.pos = carve(Bm * 4); o.status = carve(16);
+  o.params = carve(sizeof(SampleParams)); o.done = carve(16);
+  for (int g = 64; g <= persistent_max_grid() && !o.persist_shape; g += 8)
+    o.persist_shape = persistent_decode_supported(cfg->dtype, cfg->n_embd, H,
+                                                  cfg->n_layer, Tb, 1, g);
+  if (o.persist_shape) {
+    const size_t L = cfg->n_layer, SL = (size_t)persistent_exchange_slack();
+    o.eq = carve((L * 3 * C + SL) * 8);
+    o.er = carve((L * H * (size_t)nchunk * (hs + 2) + SL) * 8);
+    o.ey = carve((L * C + SL) * 8);
+    o.e1 = carve((L * C + SL) * 8);
+    o.ef = carve((L * 4 * C + SL) * 8);
+    o.e2 = carve((L * C + SL) * 8);
+    o.epoch = carve(16);
+    o.ecand = carve((2 * (size_t)persistent_max_grid() + SL) * 8);
+    o.dlayers = carve(L * sizeof(PersistLayer));
+  }
+  o.total = off;
+  return o;
+}
+
+static int check_weights(const ngpt_config* cfg, const ngpt_weights* w) {
   if (!w || !w->wte || !w->wpe || !w->lnf_w || (cfg->n_layer > 0 && !w->layers))
     return fail(nullptr, NGPT_E_ARG, "missing weight pointer");
   const bool bias = cfg->bias != 0;
@@ -211,6 +300,21 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
       if (misaligned(p)) return fail(nullptr, NGPT_E_ARG, "weights must be 16-byte aligned");
     }
   }
+  return NGPT_OK;
+}
+
+// Build a handle over a workspace the caller (or the library's static
+// array) provides.  Enqueues the zero fill and the layer-table writes; no
+// allocation, no wait.
+static int create_on(const ngpt_config* cfg, const ngpt_weights* w, void* ws,
+                     size_t ws_bytes, void* stream, ngpt_model** out) {
+  *out = nullptr;
+  const WsLayout o = ws_layout(cfg);
+  if (!ws) return fail(nullptr, NGPT_E_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(nullptr, NGPT_E_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < o.total)
+    return fail(nullptr, NGPT_E_SIZE, "workspace smaller than ngpt_workspace_bytes(cfg)");
 
   ngpt_model* m = new ngpt_model();
   m->cfg = *cfg;
@@ -222,94 +326,64 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
   m->wte = w->wte; m->wpe = w->wpe; m->lnf_w = w->lnf_w; m->lnf_b = w->lnf_b;
   m->layers.assign(w->layers, w->layers + m->L);
   m->stream = static_cast<hipStream_t>(stream);
+  m->ws = ws;
+  m->ws_bytes = o.total;
 
-  const size_t Mm = m->Mmax, Bm = cfg->max_batch, C = m->C, es = m->esz;
-  size_t off = 0;
-  auto carve = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  const size_t o_x = carve(Mm * C * 4), o_h = carve(Mm * C * es),
-               o_q = carve(Mm * C * es), o_y = carve(Mm * C * es),
-               o_f = carve(Mm * 4 * C * es), o_z = carve(Bm * C * es),
-               o_lg = carve(Bm * (size_t)m->V * 4), o_rb = carve(Mm * 4),
-               o_rp = carve(Mm * 4), o_lr = carve(Bm * 4),
-               o_part = carve(Bm * m->H * (size_t)m->nchunk * (m->hs + 2) * 4),
-               o_ppart = carve((size_t)m->H * m->Tb * attn_prefill_split_chunks(m->Tb) *
-                               (m->hs + 4) * 4),
-               o_tok = carve(Bm * 4),
-               o_pos = carve(Bm * 4), o_st = carve(16),
-               o_prm = carve(sizeof(SampleParams));
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess) cus = 0;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  }
-  // One-launch decode grid: the fewest workgroups (a multiple of 8, at most
-  // one per CU) whose register slabs hold every phase's rows.  Each exchange
-  // waits for words from all workgroups, and that wait shortens with fewer
-  // participants (measured: 245 us per GPT-2-small step at 192 workgroups,
-  // 260 at 224, 265 at 256).
-  int pgrid = 0;
-  for (int g = 64; g <= cus && pgrid == 0; g += 8)
-    if (persistent_decode_supported(cfg->dtype, m->C, m->H, m->L, m->Tb, 1, g)) pgrid = g;
+  char* base = static_cast<char*>(ws);
+  m->x = (float*)(base + o.x); m->h = base + o.h; m->q = base + o.q;
+  m->y = base + o.y; m->f = base + o.f; m->z = base + o.z;
+  m->logits = (float*)(base + o.logits);
+  m->row_b = (int32_t*)(base + o.row_b); m->row_pos = (int32_t*)(base + o.row_pos);
+  m->last_rows = (int32_t*)(base + o.last_rows); m->part = (float*)(base + o.part);
+  m->ppart = (float*)(base + o.ppart);
+  m->d_ids = (int32_t*)(base + o.ids);
+  m->tok = (int32_t*)(base + o.tok);
+  m->pos = (int32_t*)(base + o.pos); m->status = (int32_t*)(base + o.status);
+  m->params = (SampleParams*)(base + o.params);
+  m->done = (uint32_t*)(base + o.done);
+
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int pgrid = o.persist_shape
+                        ? persistent_pick_grid(cfg->dtype, m->C, m->H, m->L, m->Tb, cus)
+                        : 0;
   m->persist_grid = pgrid;
   m->persist = pgrid > 0;
-  const size_t L = m->L, SL = (size_t)persistent_exchange_slack();
-  const size_t o_eq = m->persist ? carve((L * 3 * C + SL) * 8) : 0,
-               o_er = m->persist ? carve((L * m->H * (size_t)m->nchunk * (m->hs + 2) + SL) * 8) : 0,
-               o_ey = m->persist ? carve((L * C + SL) * 8) : 0,
-               o_e1 = m->persist ? carve((L * C + SL) * 8) : 0,
-               o_ef = m->persist ? carve((L * 4 * C + SL) * 8) : 0,
-               o_e2 = m->persist ? carve((L * C + SL) * 8) : 0,
-               o_ep = m->persist ? carve(16) : 0,
-               o_ec = m->persist ? carve((2 * (size_t)pgrid + SL) * 8) : 0,
-               o_dl = m->persist ? carve(L * sizeof(PersistLayer)) : 0;
-  hipError_t e = hipMalloc(&m->ws, off);
-  if (e != hipSuccess) {
-    delete m;
-    return fail(nullptr, NGPT_E_HIP, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
+  if (o.persist_shape) {
+    m->e_qkv = (uint64_t*)(base + o.eq); m->e_rec = (uint64_t*)(base + o.er);
+    m->e_y = (uint64_t*)(base + o.ey); m->e_x1 = (uint64_t*)(base + o.e1);
+    m->e_f = (uint64_t*)(base + o.ef); m->e_x2 = (uint64_t*)(base + o.e2);
+    m->epoch = (uint32_t*)(base + o.epoch);
+    m->e_cand = (uint64_t*)(base + o.ecand);
+    m->d_layers = (PersistLayer*)(base + o.dlayers);
   }
-  char* base = static_cast<char*>(m->ws);
-  m->x = (float*)(base + o_x); m->h = base + o_h; m->q = base + o_q;
-  m->y = base + o_y; m->f = base + o_f; m->z = base + o_z;
-  m->logits = (float*)(base + o_lg);
-  m->row_b = (int32_t*)(base + o_rb); m->row_pos = (int32_t*)(base + o_rp);
-  m->last_rows = (int32_t*)(base + o_lr); m->part = (float*)(base + o_part);
-  m->ppart = (float*)(base + o_ppart);
-  m->tok = (int32_t*)(base + o_tok);
-  m->pos = (int32_t*)(base + o_pos); m->status = (int32_t*)(base + o_st);
-  m->params = (SampleParams*)(base + o_prm);
-  std::vector<PersistLayer> hl;
+
+  hipStream_t s = m->stream;
+  zero_kernel<<<1024, 256, 0, s>>>(static_cast<uint4*>(ws), o.total / 16);
+  set_params_kernel<<<1, 64, 0, s>>>(m->params, m->h_params);
   if (m->persist) {
-    m->e_qkv = (uint64_t*)(base + o_eq); m->e_rec = (uint64_t*)(base + o_er);
-    m->e_y = (uint64_t*)(base + o_ey); m->e_x1 = (uint64_t*)(base + o_e1);
-    m->e_f = (uint64_t*)(base + o_ef); m->e_x2 = (uint64_t*)(base + o_e2);
-    m->epoch = (uint32_t*)(base + o_ep);
-    m->e_cand = (uint64_t*)(base + o_ec);
-    m->d_layers = (PersistLayer*)(base + o_dl);
-    for (const ngpt_layer_weights& lw : m->layers)
-      hl.push_back(PersistLayer{(const bf16_t*)lw.ln1_w, (const bf16_t*)lw.ln1_b,
-                                (const bf16_t*)lw.attn_w, (const bf16_t*)lw.attn_b,
-                                (const bf16_t*)lw.attnproj_w, (const bf16_t*)lw.attnproj_b,
-                                (const bf16_t*)lw.ln2_w, (const bf16_t*)lw.ln2_b,
-                                (const bf16_t*)lw.fc_w, (const bf16_t*)lw.fc_b,
-                                (const bf16_t*)lw.mlpproj_w, (const bf16_t*)lw.mlpproj_b});
+    for (int l0 = 0; l0 < m->L; l0 += kTableChunk) {
+      LayerTableChunk c{};
+      c.first = l0;
+      c.n = std::min(kTableChunk, m->L - l0);
+      for (int i = 0; i < c.n; ++i) {
+        const ngpt_layer_weights& lw = m->layers[l0 + i];
+        c.l[i] = PersistLayer{(const bf16_t*)lw.ln1_w, (const bf16_t*)lw.ln1_b,
+                              (const bf16_t*)lw.attn_w, (const bf16_t*)lw.attn_b,
+                              (const bf16_t*)lw.attnproj_w, (const bf16_t*)lw.attnproj_b,
+                              (const bf16_t*)lw.ln2_w, (const bf16_t*)lw.ln2_b,
+                              (const bf16_t*)lw.fc_w, (const bf16_t*)lw.fc_b,
+                              (const bf16_t*)lw.mlpproj_w, (const bf16_t*)lw.mlpproj_b};
+      }
+      set_layer_table_kernel<<<1, 64, 0, s>>>(m->d_layers, c);
+    }
   }
-  e = hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipMemsetAsync(m->ws, 0, off, m->stream);
-  SampleParams p{1.0f, 0, 1, 0};
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(m->params, &p, sizeof(p), hipMemcpyHostToDevice, m->stream);
-  if (e == hipSuccess && m->persist)
-    e = hipMemcpyAsync(m->d_layers, hl.data(), hl.size() * sizeof(PersistLayer),
-                       hipMemcpyHostToDevice, m->stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    std::string msg = std::string("workspace init: ") + hipGetErrorString(e);
-    if (m->cap) (void)hipStreamDestroy(m->cap);
-    (void)hipFree(m->ws);
     delete m;
-    return fail(nullptr, NGPT_E_HIP, msg);
+    return fail(nullptr, NGPT_E_HIP, std::string("workspace init: ") + hipGetErrorString(e));
   }
   *out = m;
   return NGPT_OK;
@@ -321,17 +395,42 @@ static void drop_graph(GraphSlot& g) {
   g = GraphSlot();
 }
 
-int ngpt_destroy(ngpt_model* m) {
-  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+static int release(ngpt_model* m) {
   hipError_t e = hipStreamSynchronize(m->stream);
   drop_graph(m->g_step);
   drop_graph(m->g_feed);
   if (m->cap) (void)hipStreamDestroy(m->cap);
-  if (m->ws) (void)hipFree(m->ws);
+  for (hipEvent_t ev : m->pinned_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  if (m->pinned) (void)hipHostFree(m->pinned);
   delete m;
   if (e != hipSuccess)
     return fail(nullptr, NGPT_E_HIP, std::string("destroy: ") + hipGetErrorString(e));
   return NGPT_OK;
+}
+
+extern "C" {
+
+size_t ngpt_workspace_bytes(const ngpt_config* cfg) {
+  if (check_config(cfg, nullptr) != NGPT_OK) return 0;
+  return ws_layout(cfg).total;
+}
+
+int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* workspace,
+                size_t ws_bytes, void* stream, ngpt_model** out) {
+  if (!out) return fail(nullptr, NGPT_E_ARG, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  int rc = check_config(cfg, &why);
+  if (rc != NGPT_OK) return fail(nullptr, rc, why);
+  rc = check_weights(cfg, w);
+  if (rc != NGPT_OK) return rc;
+  return create_on(cfg, w, workspace, ws_bytes, stream, out);
+}
+
+int ngpt_destroy(ngpt_model* m) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  return release(m);
 }
 
 int ngpt_set_wait_limit(ngpt_model* m, int32_t passes) {
@@ -347,14 +446,16 @@ int ngpt_set_sampling(ngpt_model* m, float temperature, int32_t top_k, int32_t g
   if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
   if (!greedy && !(temperature > 0.f))
     return fail(m, NGPT_E_ARG, "temperature must be > 0 unless greedy");
-  // The parameters live in device memory read by the sampler kernel; the
-  // copy is ordered on the stream and waited for, so the host value can go.
+  // The parameters live in device memory read by the sampler kernel; they
+  // are written by a kernel on the stream, ordered after earlier work.
   SampleParams p{temperature, top_k, greedy ? 1 : 0, 0};
-  HIP_TRY(m, hipMemcpyAsync(m->params, &p, sizeof(p), hipMemcpyHostToDevice, m->stream));
-  HIP_TRY(m, hipStreamSynchronize(m->stream));
+  set_params_kernel<<<1, 64, 0, m->stream>>>(m->params, p);
+  HIP_TRY(m, hipGetLastError());
   m->h_params = p;
   return NGPT_OK;
 }
+
+}  // extern "C"
 
 static int check_kv(ngpt_model* m, const ngpt_kv* kv) {
   if (!kv || !kv->k || !kv->v || !kv->lens || !kv->limit)
@@ -366,25 +467,29 @@ static int check_kv(ngpt_model* m, const ngpt_kv* kv) {
   return NGPT_OK;
 }
 
+static bool same_kv(const ngpt_kv& a, const ngpt_kv& b) {
+  return a.k == b.k && a.v == b.v && a.lens == b.lens && a.limit == b.limit &&
+         a.batch == b.batch;
+}
+
 static void* layer_cache(const ngpt_model* m, void* base, int l, int kvB) {
   return static_cast<char*>(base) +
          (size_t)l * kvB * m->H * m->Tb * m->hs * m->esz;
 }
 
-int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
-                 const int32_t* lens, const int32_t* limit, int32_t B,
-                 int32_t Tmax) {
-  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+// Host checks shared by both prefill entry points; fills the row map and
+// the lens/limit record.
+static int plan_prefill(ngpt_model* m, const ngpt_kv* kv, const int32_t* lens,
+                        const int32_t* limit, int32_t B, int32_t Tmax, RowMap& map,
+                        LensArgs& la, int& maxlen) {
   int rc = check_kv(m, kv);
   if (rc != NGPT_OK) return rc;
-  if (!ids || !lens) return fail(m, NGPT_E_ARG, "ids or lens is NULL");
+  if (!lens) return fail(m, NGPT_E_ARG, "lens is NULL");
   if (B < 1 || B > kv->batch) return fail(m, NGPT_E_ARG, "B must be in [1, kv->batch]");
-  RowMap map{};
   map.B = B;
-  LensArgs la{};
   la.n = kv->batch;
   long total = 0;
-  int maxlen = 0;
+  maxlen = 0;
   for (int b = 0; b < B; ++b) {
     const int lb = lens[b];
     const int lim = limit ? limit[b] : m->Tb;
@@ -401,8 +506,14 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
   if (total > m->cfg.max_prefill_tokens)
     return fail(m, NGPT_E_SIZE, "sum(lens) > max_prefill_tokens");
   for (int b = B; b < kv->batch; ++b) { la.lens[b] = 0; la.limit[b] = 0; }
+  return NGPT_OK;
+}
 
-  const int M = (int)total, C = m->C, dt = m->cfg.dtype;
+// The prefill launch sequence.  ids: device; Tmax > 0 gives the [B][Tmax]
+// right-padded layout, Tmax == 0 the packed layout (row r of the map).
+static int enqueue_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
+                           const RowMap& map, const LensArgs& la, int maxlen) {
+  const int M = map.off[map.B], C = m->C, dt = m->cfg.dtype, B = map.B;
   hipStream_t s = m->stream;
   m->cand_ok = false;   // the logits are about to come from this prefill
   set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(la, kv->lens, kv->limit);
@@ -439,11 +550,69 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
 
+  m->rec_kv = *kv;
   m->h_lens.assign(kv->batch, 0);
   m->h_limit.assign(kv->batch, 0);
   for (int b = 0; b < B; ++b) { m->h_lens[b] = la.lens[b]; m->h_limit[b] = la.limit[b]; }
   return NGPT_OK;
 }
+
+extern "C" {
+
+int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
+                 const int32_t* lens, const int32_t* limit, int32_t B,
+                 int32_t Tmax) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  if (!ids) return fail(m, NGPT_E_ARG, "ids is NULL");
+  RowMap map{};
+  LensArgs la{};
+  int maxlen = 0;
+  int rc = plan_prefill(m, kv, lens, limit, B, Tmax, map, la, maxlen);
+  if (rc != NGPT_OK) return rc;
+  // every id on the host, before anything is enqueued
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < lens[b]; ++p) {
+      const int32_t id = ids[(size_t)b * Tmax + p];
+      if (id < 0 || id >= m->V)
+        return fail(m, NGPT_E_RANGE, "prompt id outside [0, vocab_size)");
+    }
+  // pinned staging, packed, then an asynchronous copy to the workspace
+  const size_t half = (size_t)m->cfg.max_prefill_tokens;
+  if (!m->pinned) {
+    HIP_TRY(m, hipHostMalloc(reinterpret_cast<void**>(&m->pinned), 2 * half * sizeof(int32_t),
+                             hipHostMallocDefault));
+    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[0], hipEventDisableTiming));
+    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[1], hipEventDisableTiming));
+  }
+  const int hf = m->pinned_half;
+  if (m->pinned_used[hf]) HIP_TRY(m, hipEventSynchronize(m->pinned_ev[hf]));
+  int32_t* stage = m->pinned + hf * half;
+  for (int b = 0; b < B; ++b)
+    memcpy(stage + map.off[b], ids + (size_t)b * Tmax, sizeof(int32_t) * lens[b]);
+  const int M = map.off[B];
+  HIP_TRY(m, hipMemcpyAsync(m->d_ids, stage, sizeof(int32_t) * M, hipMemcpyHostToDevice,
+                            m->stream));
+  HIP_TRY(m, hipEventRecord(m->pinned_ev[hf], m->stream));
+  m->pinned_used[hf] = true;
+  m->pinned_half = hf ^ 1;
+  return enqueue_prefill(m, kv, m->d_ids, 0, map, la, maxlen);
+}
+
+int ngpt_prefill_device(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
+                        const int32_t* lens, const int32_t* limit, int32_t B,
+                        int32_t Tmax) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  if (!ids) return fail(m, NGPT_E_ARG, "ids is NULL");
+  if (Tmax < 1) return fail(m, NGPT_E_ARG, "Tmax must be >= 1");
+  RowMap map{};
+  LensArgs la{};
+  int maxlen = 0;
+  int rc = plan_prefill(m, kv, lens, limit, B, Tmax, map, la, maxlen);
+  if (rc != NGPT_OK) return rc;
+  return enqueue_prefill(m, kv, ids, Tmax, map, la, maxlen);
+}
+
+}  // extern "C"
 
 // The one-token forward shared by the step and feed graphs.  The head node
 // (sampler or feed) has already set tok/pos, advanced lens and written the
@@ -457,7 +626,7 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   a.layers = m->d_layers;
   a.pos = m->pos;
   a.fused = 0;
-  a.lens = kv->lens; a.tok = m->tok; a.next_ids = nullptr;
+  a.lens = kv->lens; a.limit = kv->limit; a.tok = m->tok; a.next_ids = nullptr;
   a.e_cand = m->e_cand;
   a.x0 = m->x;
   a.kc = (bf16_t*)kv->k; a.vc = (bf16_t*)kv->v;
@@ -465,7 +634,8 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   a.logits = m->logits;
   a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
   a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
-  a.epoch = m->epoch; a.status = m->status; a.wait_limit = m->h_wait_limit;
+  a.epoch = m->epoch; a.done = m->done; a.status = m->status;
+  a.wait_limit = m->h_wait_limit;
   return a;
 }
 
@@ -536,6 +706,7 @@ static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
 static int capture(ngpt_model* m, GraphSlot& g, const ngpt_kv* kv, int mode,
                    const void* arg_in, int32_t* arg_out) {
   drop_graph(g);
+  if (!m->cap) HIP_TRY(m, hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking));
   hipStream_t s = m->cap;
   HIP_TRY(m, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
   const SamplerArgs a = head_args(m, kv, mode, arg_in, arg_out);
@@ -571,8 +742,10 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
                     const void* arg_in, int32_t* arg_out) {
   int rc = check_kv(m, kv);
   if (rc != NGPT_OK) return rc;
-  if ((int)m->h_lens.size() != kv->batch)
-    return fail(m, NGPT_E_ARG, "kv batch differs from the last prefill");
+  // the host record of lens / limit and the greedy candidates belong to the
+  // cache of the last prefill
+  if (m->h_lens.empty() || !same_kv(*kv, m->rec_kv))
+    return fail(m, NGPT_E_ARG, "kv is not the cache of the last prefill on this model");
   bool any = false;
   for (int b = 0; b < kv->batch; ++b) any |= m->h_lens[b] < m->h_limit[b];
   if (!any) return fail(m, NGPT_E_CONTEXT, "no sequence can take another token");
@@ -588,10 +761,10 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
     if (m->h_lens[0] < m->h_limit[0]) ++m->h_lens[0];
     return NGPT_OK;
   }
-  const bool same_kv = g.exec && g.k == kv->k && g.v == kv->v &&
-                       g.lens == kv->lens && g.limit == kv->limit &&
-                       g.batch == kv->batch && g.wait_limit == m->h_wait_limit;
-  if (!same_kv) {
+  const bool same = g.exec && g.k == kv->k && g.v == kv->v &&
+                    g.lens == kv->lens && g.limit == kv->limit &&
+                    g.batch == kv->batch && g.wait_limit == m->h_wait_limit;
+  if (!same) {
     rc = capture(m, g, kv, mode, arg_in, arg_out);
     if (rc != NGPT_OK) return rc;
   } else if (g.arg_in != arg_in || g.arg_out != arg_out) {
@@ -609,6 +782,8 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
     if (m->h_lens[b] < m->h_limit[b]) ++m->h_lens[b];
   return NGPT_OK;
 }
+
+extern "C" {
 
 int ngpt_decode_step(ngpt_model* m, ngpt_kv* kv, int32_t* next_ids,
                      const double* uniforms) {
@@ -667,14 +842,8 @@ int ngpt_copy_logits(ngpt_model* m, float* dst, int32_t ld_dst, int32_t B) {
 
 int ngpt_device_status(ngpt_model* m, int32_t* status) {
   if (!m || !status) return fail(m, NGPT_E_ARG, "NULL argument");
-  int32_t v = 0;
-  HIP_TRY(m, hipStreamSynchronize(m->stream));
-  HIP_TRY(m, hipMemcpy(&v, m->status, sizeof(v), hipMemcpyDeviceToHost));
-  clear_status_kernel<<<1, 64, 0, m->stream>>>(m->status);
+  read_status_kernel<<<1, 64, 0, m->stream>>>(m->status, status);
   HIP_TRY(m, hipGetLastError());
-  HIP_TRY(m, hipStreamSynchronize(m->stream));
-  // bit 2: a one-launch decode wait gave up; bit 1: an id out of range
-  *status = (v & 2) ? NGPT_E_TIMEOUT : v ? NGPT_E_DEVICE : NGPT_OK;
   return NGPT_OK;
 }
 

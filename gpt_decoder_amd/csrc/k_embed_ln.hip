@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void embed_prefill_kernel(
   }
   const int b = lo;
   const int p = r - map.off[b];
-  int id = ids[(size_t)b * Tmax + p];
+  int id = ids[Tmax > 0 ? (size_t)b * Tmax + p : (size_t)r];
   if (id < 0 || id >= V) {
     if (threadIdx.x == 0) atomicOr(status, 1);
     id = 0;

@@ -578,15 +578,16 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
         int bi = INT_MAX;
         for (int k = lane; k < G; k += 64) cand_take(bv, bi, bCand[2 * k], __float_as_int(bCand[2 * k + 1]));
         cand_wave(bv, bi);
-        const int tok = bi;
+        // a row with no finite maximum (bi == INT_MAX) gives id 0 and the
+        // invalid-input flag, the sampler's rule
         const int sl = tid - 64 * kCompute;
-        if (tok >= 0 && tok < a.V) {
+        const bool bad = !(bi >= 0 && bi < a.V);
+        const int tok = bad ? 0 : bi;
+        if (bad && w == 0 && sl == 0) atomicOr(a.status, 1);
+        {
           const bf16_t* te = a.wte + (size_t)tok * C;
           const bf16_t* pe = a.wpe + (size_t)p * C;
           for (int c = sl; c < C; c += kSyncLanes) bX[c] = to_f32(te[c]) + to_f32(pe[c]);
-        } else {
-          for (int c = sl; c < C; c += kSyncLanes) bX[c] = 0.f;
-          if (sl == 0) atomicOr(a.status, 1);
         }
         if (w == 0 && sl == 0) {
           a.next_ids[0] = tok;
@@ -839,9 +840,18 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ PShared S;
   const uint32_t ep = *a.epoch + 1u;
-  // position of the new token: the sampler head node has set pos, or, in a
-  // fused greedy step, the current length (advanced at the end)
-  const int p = a.fused ? a.lens[0] : a.pos[0];
+  // position of the new token: the sampler head node has set pos (< 0:
+  // inactive), or, in a fused greedy step, the current length (advanced at
+  // the end) while it is below the sequence's limit
+  int p = a.pos[0];
+  if (a.fused) {
+    p = a.lens[0];
+    if (p >= a.limit[0]) p = -1;
+    if (p < 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+      a.next_ids[0] = -1;
+      a.pos[0] = -1;
+    }
+  }
   if (threadIdx.x == 0) S.fail = INT_MAX;
   if (threadIdx.x < kCompute) { S.cv[threadIdx.x] = -INFINITY; S.ci[threadIdx.x] = INT_MAX; }
   __syncthreads();
@@ -856,20 +866,30 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
     else
       run_role<false>(a, smem, S, ep, p);
   }
-  // the epoch advances once per launch; workgroup 0 finishes last among
-  // the readers of the old value (its final phase waits for every block)
   __syncthreads();
-  // this workgroup's greedy candidate for the next launch
-  if (threadIdx.x == 0 && p >= 0) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int i = 0; i < kCompute; ++i) cand_take(bv, bi, S.cv[i], S.ci[i]);
-    tag_store(a.e_cand + 2 * blockIdx.x, bv, ep);
-    tag_store(a.e_cand + 2 * blockIdx.x + 1, __int_as_float(bi), ep);
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (a.fused && S.fail == INT_MAX) a.lens[0] = p + 1;
-    *a.epoch = ep;
+  if (threadIdx.x == 0) {
+    // this workgroup's greedy candidate for the next launch, only from a
+    // launch whose waits all completed here
+    if (p >= 0 && S.fail == INT_MAX) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      for (int i = 0; i < kCompute; ++i) cand_take(bv, bi, S.cv[i], S.ci[i]);
+      tag_store(a.e_cand + 2 * blockIdx.x, bv, ep);
+      tag_store(a.e_cand + 2 * blockIdx.x + 1, __int_as_float(bi), ep);
+    }
+    if (blockIdx.x == 0 && a.fused && p >= 0 && S.fail == INT_MAX) a.lens[0] = p + 1;
+    // The epoch advances once per launch, by the last workgroup to finish:
+    // every workgroup has read the old value before it arrives here, also
+    // when a wait timed out or the grid was not all resident, so no
+    // workgroup of this launch can tag a word with the next launch's epoch.
+    // (relaxed: the epoch was read at the start and used by every wait
+    // since, and a fence here would write back this XCD's L2)
+    const uint32_t prev = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.epoch, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -893,6 +913,30 @@ bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,
 }
 
 size_t persistent_lds_bytes(int C, int L) { return (size_t)lds_floats(C, L) * sizeof(float); }
+
+int persistent_max_grid() { return kMaxGrid; }
+
+int persistent_blocks_per_cu(int C, int L) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(decode_persistent_kernel), kThreads,
+          persistent_lds_bytes(C, L)) != hipSuccess)
+    return 0;
+  return n;
+}
+
+// Each exchange waits for words from all workgroups, and that wait shortens
+// with fewer participants (measured: 245 us per GPT-2-small step at 192
+// workgroups, 260 at 224, 265 at 256), so the grid is the fewest workgroups
+// that hold the rows.  Every workgroup must be resident at once (the phases
+// wait on each other), which the occupancy query confirms.
+int persistent_pick_grid(int dtype, int C, int H, int L, int Tb, int cus) {
+  int g = 0;
+  for (int t = 64; t <= (cus < kMaxGrid ? cus : kMaxGrid) && g == 0; t += 8)
+    if (persistent_decode_supported(dtype, C, H, L, Tb, 1, t)) g = t;
+  if (g > 0 && (long)persistent_blocks_per_cu(C, L) * cus < g) g = 0;
+  return g;
+}
 
 int persistent_exchange_slack() { return 512; }
 

@@ -118,7 +118,7 @@ __device__ int row_argmax(const float* lg, int V, SampShared& sh) {
   __syncthreads();
   int r = 0x7FFFFFFF;
   for (int i = 0; i < kSampThreads / 64; ++i) r = min(r, sh.ired[i]);
-  return r == 0x7FFFFFFF ? 0 : r;
+  return r;   // 0x7FFFFFFF: no finite maximum (all -inf or NaN)
 }
 
 __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
@@ -248,9 +248,15 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
   } else {
     const SampleParams p = *prm;
     const float* lg = logits + (size_t)b * ld;
-    if (p.greedy)
+    if (p.greedy) {
+      // a row with no finite maximum gives id 0 and the invalid-input flag
+      // (the same rule as the one-launch decode kernel's greedy pick)
       id = row_argmax(lg, V, sh);
-    else
+      if (id == 0x7FFFFFFF) {
+        if (threadIdx.x == 0) atomicOr(status, 1);
+        id = 0;
+      }
+    } else
       id = row_sample(lg, V, p.temperature, p.top_k, uniforms[b], sh);
   }
   if (threadIdx.x == 0) {

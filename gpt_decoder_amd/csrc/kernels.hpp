@@ -53,6 +53,7 @@ enum SampleMode {
   FEED_STEP = 2,    // teacher forcing: ids given, set tok/pos, advance lens
 };
 
+// ids: [B][Tmax] right-padded (Tmax > 0) or packed by row (Tmax == 0)
 void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
                           const RowMap& map, int M, const void* wte,
                           const void* wpe, int C, int V, float* x,
@@ -144,41 +145,6 @@ void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
 // sets tok/pos, advances lens and writes the row's embedding.
 void launch_sampler(const SamplerArgs& a, int B, hipStream_t s);
 
-// ---------------------------------------------------------------------------
-// One-launch decode step for batch 1 (bf16, head size 64, n_embd <= 768).
-struct PersistLayer {
-  const bf16_t *ln1_w, *ln1_b, *attn_w, *attn_b, *proj_w, *proj_b;
-  const bf16_t *ln2_w, *ln2_b, *fc_w, *fc_b, *mp_w, *mp_b;
-};
-
-struct PersistArgs {
-  int L, H, C, V, Tb, nchunk;
-  const bf16_t *wte, *wpe, *lnf_w, *lnf_b;
-  const PersistLayer* layers;   // device array [L]
-  int32_t* pos;                 // [1]: set by the head node (< 0: inactive),
-                                // or written here in a fused greedy step
-  int fused;                    // 1: greedy step without a head node
-  int32_t* lens;                // kv lens [1] (fused: read, then advanced)
-  int32_t* tok;                 // fused: the chosen id ...
-  int32_t* next_ids;            // ... and the caller's copy
-  uint64_t* e_cand;             // greedy candidates, 2 words per workgroup
-  const float* x0;              // [C] embedding written by the head node
-  bf16_t* kc;                   // cache bases and per-layer stride (elements)
-  bf16_t* vc;
-  size_t layer_stride;
-  float* logits;                // [V]
-  // exchange words (fp32 value | epoch << 32), per layer
-  uint64_t *e_qkv, *e_rec, *e_y, *e_x1, *e_f, *e_x2;
-  uint32_t* epoch;              // advanced once per launch
-  int32_t* status;              // bit 2: a wait timed out
-  int wait_limit;                // poll passes before a wait gives up (0: default)
-};
-
-bool persistent_decode_supported(int dtype, int C, int H, int L, int Tb,
-                                 int batch, int grid);
-size_t persistent_lds_bytes(int C, int L);
-// words of slack past the end of each exchange buffer (polls read ahead)
-int persistent_exchange_slack();
-void launch_decode_persistent(const PersistArgs& a, int grid, hipStream_t s);
-
 }  // namespace ngpt
+
+#include "k_persist.hpp"

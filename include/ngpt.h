@@ -14,8 +14,9 @@
  *   - serving page "原生 nanoGPT 模型服务首选": section 1 (LayerNorm with an
  *     optional bias), section 2 (generate(): last-position logits / T,
  *     top-k filter, softmax, multinomial, append), and the KV-cache section
- *     (c_attn split into q, k, v; past K/V concatenated along time; only the
- *     newest token is fed; causal masking only without a past).
+ *     "一个值得做的改进" (c_attn split into q, k, v; past K/V concatenated
+ *     along time; only the newest token is fed; causal masking only without
+ *     a past).
  *   - SDK guide "极速上手nanoGPT", "模型架构解析" (GPTConfig fields and defaults,
  *     scaled masked softmax attention).
  *   - architecture analysis "nanoGPT 架构分析", section 4.1 (pre-LN blocks,
@@ -26,12 +27,13 @@
  * Conventions
  *   - Every call returns an int status (NGPT_OK = 0, negative on error); no
  *     exception crosses the ABI.  ngpt_last_error() gives a message.
- *   - Work is enqueued asynchronously on the stream given to ngpt_create();
- *     calls do not synchronise unless stated.
- *   - Weights and KV buffers are caller-owned device memory and are borrowed:
- *     they must stay alive and unmodified while the model uses them.  The
- *     library owns only its workspace (allocated in ngpt_create, freed in
- *     ngpt_destroy).
+ *   - Work is enqueued asynchronously on the stream given to ngpt_create().
+ *     No call synchronises the stream except ngpt_destroy(); the only host
+ *     waits are the ones stated (ngpt_prefill reusing its pinned staging).
+ *   - All device memory is caller-owned and borrowed: weights, the KV cache
+ *     and the workspace (sized by ngpt_workspace_bytes()) must stay alive and
+ *     unmodified by others while the model uses them.  The library never
+ *     allocates device memory.
  *   - A handle is bound to one stream and is not thread-safe.
  *   - Element type of every weight, bias, LayerNorm parameter and KV entry is
  *     the config dtype (fp32 or bf16).  The residual stream, LayerNorm
@@ -52,10 +54,11 @@ extern "C" {
 #define NGPT_E_ARG       -1  /* NULL pointer, inconsistent argument        */
 #define NGPT_E_CONFIG    -2  /* unsupported model shape or dtype           */
 #define NGPT_E_RANGE     -3  /* a token id or a length outside its range   */
-#define NGPT_E_SIZE      -4  /* batch or token count above the create-time bound */
+#define NGPT_E_SIZE      -4  /* batch, token count or buffer size out of bounds */
 #define NGPT_E_CONTEXT   -5  /* no sequence can take another token          */
 #define NGPT_E_HIP       -6  /* a HIP runtime call failed                   */
-#define NGPT_E_DEVICE    -7  /* a kernel reported an out-of-range id        */
+#define NGPT_E_DEVICE    -7  /* a kernel saw invalid input (id out of range,
+                                or a logits row with no finite maximum)    */
 #define NGPT_E_TIMEOUT   -8  /* a wait in the one-launch decode kernel gave up */
 
 /* Element types. */
@@ -63,7 +66,7 @@ extern "C" {
 #define NGPT_BF16  1
 
 /*
- * Model shape, the GPTConfig of the SDK guide ("模型架构解析"): block_size,
+ * Model shape: the GPTConfig of the SDK guide ("模型架构解析"): block_size,
  * vocab_size, n_layer, n_head, n_embd, bias.  dropout is absent (inference).
  * Supported: n_embd % n_head == 0; head_dim = n_embd / n_head in {32, 64};
  * n_embd % 64 == 0 (bf16) or n_embd % 4 == 0 (fp32); n_embd <= 2048;
@@ -88,13 +91,15 @@ typedef struct {
 } ngpt_config;
 
 /*
- * Weights of one block, device pointers in nn.Linear layout
- * [out_features][in_features], row-major, elements of the config dtype.
- * attn_w is c_attn, [3C][C]: rows [0,C) give q, [C,2C) k, [2C,3C) v; head j
- * of each is the row slice [j*hs, (j+1)*hs) (serving page, KV-cache section).
- * attnproj_w is the attention c_proj [C][C]; fc_w is [4C][C]; mlpproj_w is
- * [C][4C].  LayerNorm weights are [C].  Bias pointers must all be NULL when
- * bias == 0 and all non-NULL when bias == 1 (serving page, section 1).
+ * Weights of one block (SDK guide "模型架构解析": the Block of ln_1, attn
+ * (c_attn, c_proj), ln_2, mlp (c_fc, GELU, c_proj)), device pointers in
+ * nn.Linear layout [out_features][in_features], row-major, elements of the
+ * config dtype.  attn_w is c_attn, [3C][C]: rows [0,C) give q, [C,2C) k,
+ * [2C,3C) v; head j of each is the row slice [j*hs, (j+1)*hs) (serving
+ * page, KV-cache section).  attnproj_w is the attention c_proj [C][C]; fc_w
+ * is [4C][C]; mlpproj_w is [C][4C].  LayerNorm weights are [C].  Bias
+ * pointers must all be NULL when bias == 0 and all non-NULL when bias == 1
+ * (serving page, section 1).  Every pointer must be 16-byte aligned.
  */
 typedef struct {
   const void *ln1_w, *ln1_b;
@@ -108,8 +113,9 @@ typedef struct {
 /*
  * Whole-model weights.  wte [vocab][C] is also the lm_head (weight tying,
  * architecture analysis section 4.1), so there is no lm_head pointer and no
- * lm_head bias.  wpe is [block_size][C].  `layers` is a HOST array of
- * n_layer entries; it is copied at create time.
+ * lm_head bias.  wpe is [block_size][C] (model-building chapter, section
+ * 4.5: learned absolute positions).  `layers` is a HOST array of n_layer
+ * entries; it is copied at create time.
  */
 typedef struct {
   const void *wte, *wpe;
@@ -118,13 +124,15 @@ typedef struct {
 } ngpt_weights;
 
 /*
- * KV cache, caller-owned device memory.  k and v are each laid out
- * [n_layer][batch][n_head][block_size][head_dim] in the config dtype
- * (ngpt_kv_bytes() bytes each).  lens[b] is the number of positions of
- * sequence b held in the cache; limit[b] (<= block_size) is the total length
- * at which sequence b stops taking tokens.  Both are device int32 [batch],
- * written by ngpt_prefill() and advanced by the decode calls.  A sequence is
- * active while lens[b] < limit[b].
+ * KV cache (serving page, KV-cache section: per layer the past K and V,
+ * extended by one row per new token), caller-owned device memory.  k and v
+ * are each laid out [n_layer][batch][n_head][block_size][head_dim] in the
+ * config dtype (ngpt_kv_bytes() bytes each).  lens[b] is the number of
+ * positions of sequence b held in the cache; limit[b] (<= block_size) is
+ * the total length at which sequence b stops taking tokens.  Both are
+ * device int32 [batch], written by ngpt_prefill() and advanced by the decode
+ * calls.  A sequence is active while lens[b] < limit[b].  k and v must be
+ * 16-byte aligned.
  */
 typedef struct {
   void *k;
@@ -136,30 +144,42 @@ typedef struct {
 
 typedef struct ngpt_model ngpt_model;
 
-/* Bytes of ONE of the two KV arrays for `batch` sequences; 0 if the config is
- * invalid.  Host-only, needs no GPU. */
+/* Bytes of ONE of the two KV arrays for `batch` sequences (the KV-cache
+ * section's per-layer K and V, block_size positions each); 0 if the config
+ * is invalid or batch < 1.  Host-only, needs no GPU. */
 size_t ngpt_kv_bytes(const ngpt_config *cfg, int32_t batch);
 
-/* Validate a config without creating anything: NGPT_OK or NGPT_E_CONFIG /
- * NGPT_E_ARG.  Host-only. */
+/* Bytes of the workspace a model of this config needs (activations of up
+ * to max(max_prefill_tokens, max_batch) rows of the forward of the SDK
+ * guide's GPT class, split-K attention partials, fp32 logits
+ * [max_batch][vocab], the one-launch decode exchange buffers, counters);
+ * 0 if the config is invalid.  Host-only, needs no GPU. */
+size_t ngpt_workspace_bytes(const ngpt_config *cfg);
+
+/* Validate a config (GPTConfig fields of the SDK guide, "模型架构解析")
+ * without creating anything: NGPT_OK or NGPT_E_CONFIG / NGPT_E_ARG.
+ * Host-only. */
 int ngpt_check_config(const ngpt_config *cfg);
 
 /*
- * Create a model on the current HIP device.  `stream` is a hipStream_t
- * (NULL = the default stream) on which every later call enqueues its work.
- * Allocates the workspace (activations, split-K partials, fp32 logits
- * [max_batch][vocab]).  Sampling defaults: greedy.
- * Every weight and bias pointer must be 16-byte aligned (the kernels read
- * parameter rows with 8- and 16-byte accesses); fresh device allocations and
- * framework tensors are.
+ * Create a model (the GPT class of the SDK guide, "模型架构解析", with its
+ * weights) on the current HIP device.  `stream` is a hipStream_t (NULL =
+ * the default stream) on which every later call enqueues its work.
+ * `workspace` is caller-owned device memory of ws_bytes >=
+ * ngpt_workspace_bytes(cfg) bytes, 256-byte aligned; the library zeroes it
+ * (asynchronously, on the stream) and keeps using it until destroy.
+ * Sampling defaults: greedy.  Every weight and bias pointer must be 16-byte
+ * aligned (the kernels read parameter rows with 8- and 16-byte accesses).
  * Errors: NGPT_E_ARG (NULL pointers, bias pointers inconsistent with
- * cfg->bias, misaligned pointers), NGPT_E_CONFIG, NGPT_E_HIP.  *out is NULL
- * on error.
+ * cfg->bias, misaligned pointers), NGPT_E_CONFIG, NGPT_E_SIZE (ws_bytes too
+ * small), NGPT_E_HIP.  *out is NULL on error.
  */
-int ngpt_create(const ngpt_config *cfg, const ngpt_weights *w, void *stream,
+int ngpt_create(const ngpt_config *cfg, const ngpt_weights *w,
+                void *workspace, size_t ws_bytes, void *stream,
                 ngpt_model **out);
 
-/* Wait for the stream, then free the workspace and the handle. */
+/* Wait for the stream, then release the handle (the caller still owns the
+ * workspace, weights and KV memory).  The only call that synchronises. */
 int ngpt_destroy(ngpt_model *m);
 
 /*
@@ -170,79 +190,113 @@ int ngpt_destroy(ngpt_model *m);
  * kept ids, and the id is the smallest kept id (ascending) whose running
  * probability sum exceeds u * total for the caller's uniform u in [0,1).
  * greedy != 0 replaces all of this by the argmax (lowest id on ties) and
- * ignores the uniforms.  Takes effect for later calls; no re-capture.
+ * ignores the uniforms.  The values are written to device memory by a small
+ * kernel on the stream (no host copy, no wait); later calls see them, and no
+ * graph is captured again.  Errors: NGPT_E_ARG (temperature <= 0 unless
+ * greedy), NGPT_E_HIP.
  */
 int ngpt_set_sampling(ngpt_model *m, float temperature, int32_t top_k,
                       int32_t greedy);
 
 /*
- * Prefill: run each prompt through the model from an empty cache.
- *   ids    device int32 [B][Tmax], right-padded (entries past lens[b] ignored)
+ * Prefill (the first forward of generate(), serving page section 2, over
+ * each whole prompt; model-building chapter section 4.5 for positions 0..):
+ * run each prompt through the model from an empty cache.
+ *   ids    HOST int32 [B][Tmax], right-padded (entries past lens[b] ignored)
  *   lens   HOST int32 [B], 1 <= lens[b] <= block_size
  *   limit  HOST int32 [B] or NULL (NULL: every limit = block_size);
  *          lens[b] <= limit[b] <= block_size
+ * Every id is checked on the host (0 <= id < vocab) before anything is
+ * enqueued; the valid ids are packed into a pinned staging buffer of the
+ * handle (allocated on first use) and copied asynchronously.  Reusing that
+ * staging waits only for the copy enqueued by the previous prefill.
  * Requires B <= kv->batch <= cfg.max_batch and sum(lens) <=
  * cfg.max_prefill_tokens.  Writes K/V rows [0, lens[b]) of every layer, sets
- * kv->lens and kv->limit, and leaves the logits of position lens[b]-1 of
- * each sequence in the logits buffer.  Ids outside [0, vocab) are treated as
- * 0 by the kernel and reported by ngpt_device_status() as NGPT_E_DEVICE.
- * Errors: NGPT_E_ARG, NGPT_E_RANGE (lens/limit), NGPT_E_SIZE, NGPT_E_HIP.
+ * kv->lens and kv->limit (rows B..kv->batch-1 get lens = limit = 0, i.e.
+ * inactive), and leaves the logits of position lens[b]-1 of each sequence in
+ * the logits buffer.  Errors: NGPT_E_ARG, NGPT_E_RANGE (an id, a length or a
+ * limit out of range), NGPT_E_SIZE, NGPT_E_HIP.
  */
 int ngpt_prefill(ngpt_model *m, ngpt_kv *kv, const int32_t *ids,
                  const int32_t *lens, const int32_t *limit, int32_t B,
                  int32_t Tmax);
 
 /*
+ * ngpt_prefill() with the ids already in device memory (device int32
+ * [B][Tmax]), for callers whose tokens are produced on the GPU; no host copy.
+ * The ids cannot be checked on the host: an id outside [0, vocab) is used as
+ * 0 by the kernel and reported by ngpt_device_status() as NGPT_E_DEVICE.
+ */
+int ngpt_prefill_device(ngpt_model *m, ngpt_kv *kv, const int32_t *ids,
+                        const int32_t *lens, const int32_t *limit, int32_t B,
+                        int32_t Tmax);
+
+/*
  * One decode step for all kv->batch sequences (the loop body of generate()
- * with a KV cache): for every active b (lens[b] < limit[b]):
+ * in the serving page, section 2, with the KV cache of its "一个值得做的改进"
+ * section: only the newest token is run, against the cached K/V): for every
+ * active b (lens[b] < limit[b]):
  *   1. sample next_ids[b] from the current logits row with uniforms[b];
  *   2. run that token at position lens[b], append its K/V, refresh logits[b];
  *   3. lens[b] += 1.
  * Inactive rows get next_ids[b] = -1; their cache and logits are untouched.
  *   next_ids  device int32 [kv->batch], output
  *   uniforms  device double [kv->batch], in [0,1) (unused when greedy)
- * The step is one HIP graph launch (captured on first use for this kv;
- * re-captured if kv's pointers change; uniforms/next_ids pointers may change
- * freely).  Errors: NGPT_E_ARG, NGPT_E_CONTEXT (no active row, known from the
- * host's record of lens and limits), NGPT_E_HIP.
+ * kv must be the cache of the last prefill on this model (its pointers and
+ * batch); the host keeps a record of its lengths.  The step is one HIP graph
+ * launch or, for greedy batch-1 bf16 steps, one kernel launch; the graph is
+ * captured on first use; uniforms/next_ids pointers may change freely.
+ * Errors: NGPT_E_ARG, NGPT_E_CONTEXT (no active row, known from the host's
+ * record of lens and limits), NGPT_E_HIP.
  */
 int ngpt_decode_step(ngpt_model *m, ngpt_kv *kv, int32_t *next_ids,
                      const double *uniforms);
 
 /*
- * Teacher-forced decode step: like ngpt_decode_step() but the token of each
- * active row is given (device int32 [kv->batch]) instead of sampled.
- * Out-of-range ids are treated as 0 and reported by ngpt_device_status().
+ * Teacher-forced decode step (the same KV-cached step of the serving page,
+ * with the appended token given rather than drawn): like ngpt_decode_step()
+ * but the token of each active row is given (device int32 [kv->batch]).
+ * Out-of-range ids are used as 0 and reported by ngpt_device_status().
  */
 int ngpt_decode_feed(ngpt_model *m, ngpt_kv *kv, const int32_t *ids);
 
 /*
- * Run the sampler alone on caller logits (device fp32 [B][ld], ld >= vocab)
- * with the model's sampling parameters; writes next_ids (device int32 [B]).
- * uniforms is device double [B] (may be NULL when greedy).  No model state
- * changes.  Errors: NGPT_E_ARG, NGPT_E_SIZE (B > max_batch), NGPT_E_HIP.
+ * The sampler of generate() (serving page, section 2; rule as in
+ * ngpt_set_sampling) alone, on caller logits (device fp32 [B][ld], ld >=
+ * vocab), with the model's sampling parameters; writes next_ids (device
+ * int32 [B]).  uniforms is device double [B] (may be NULL when greedy).  No
+ * model state changes.  Taking the logits as an argument (instead of the
+ * model's own logits) lets a caller replay the draw on any row, e.g. for a
+ * bit-exact check; the model's logits are one such input (ngpt_logits).
+ * Errors: NGPT_E_ARG, NGPT_E_SIZE (B > max_batch), NGPT_E_HIP.
  */
 int ngpt_sample(ngpt_model *m, const float *logits, int32_t ld, int32_t B,
                 const double *uniforms, int32_t *next_ids);
 
 /*
- * Borrow the logits buffer: device fp32 [max_batch][ld] with ld = vocab.
- * Row b holds the logits of sequence b's last processed position.  Valid
- * until the next prefill/decode call on this model.
+ * Borrow the logits buffer (the last-position logits that generate() reads,
+ * serving page section 2): device fp32 [max_batch][ld] with ld = vocab.  Row
+ * b holds the logits of sequence b's last processed position.  Valid until
+ * the next prefill/decode call on this model.
  */
 int ngpt_logits(ngpt_model *m, const float **logits, int32_t *ld);
 
-/* Copy rows [0, B) of the logits to dst (device fp32 [B][ld_dst]),
- * asynchronously on the model's stream. */
+/* Copy rows [0, B) of the logits (as ngpt_logits) to dst (device fp32
+ * [B][ld_dst]), asynchronously on the model's stream. */
 int ngpt_copy_logits(ngpt_model *m, float *dst, int32_t ld_dst, int32_t B);
 
 /*
- * Synchronise the stream and report kernel-side input errors since the last
- * call: *status = NGPT_OK, NGPT_E_DEVICE (an id outside [0, vocab) was
- * seen) or NGPT_E_TIMEOUT (a wait inside the one-launch decode kernel gave
- * up, see ngpt_set_wait_limit: that step's ids, logits and cache rows are
- * invalid, and the sequence must be prefilled again).  A timeout is reported
- * ahead of an id error.  Clears the flags.
+ * Report kernel-side input errors since the last call, without waiting:
+ * enqueues a small kernel that writes one int32 to *status (device memory,
+ * or host memory the device can write, e.g. pinned) and clears the flags.
+ * After the stream reaches it, *status is NGPT_OK, NGPT_E_DEVICE (an id
+ * outside [0, vocab), or a greedy logits row with no finite maximum, was
+ * seen; such an id is used as 0) or NGPT_E_TIMEOUT (a wait inside the
+ * one-launch decode kernel gave up, see ngpt_set_wait_limit: that step's
+ * ids, logits and cache rows are invalid, and the sequence must be
+ * prefilled again).  A timeout is reported ahead of an id error.  This is
+ * the status path of the generate() loop (serving page, section 2), which
+ * has no error channel of its own.
  */
 int ngpt_device_status(ngpt_model *m, int32_t *status);
 
@@ -254,7 +308,8 @@ int ngpt_device_status(ngpt_model *m, int32_t *status);
  * hanging.  A small limit is a test hook that makes the timeout path run
  * (1: give up after the second pass that finds a word missing).  Takes
  * effect for later calls (a captured decode graph is captured again).
- * Errors: NGPT_E_ARG.
+ * (Not a step of the pages' method: a guard of this implementation's
+ * one-launch form of the KV-cached decode step.)  Errors: NGPT_E_ARG.
  */
 int ngpt_set_wait_limit(ngpt_model *m, int32_t passes);
 

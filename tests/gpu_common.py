@@ -35,7 +35,34 @@ def tol_for(w) -> float:
 
 
 def make_oracle(w, weights):
+    """The oracle in the precision mode of the workload's data path (bf16
+    rounding at the bf16 storage points for bf16 workloads)."""
     return oracle.OracleGPT(w, weights, act_bf16=(w.dtype == "bf16"))
+
+
+def make_exact_oracle(w, weights):
+    """The oracle evaluating the model exactly as defined (no activation
+    rounding): the bf16 path is held to the same bar against it."""
+    return oracle.OracleGPT(w, weights, act_bf16=False)
+
+
+def kv_layer_bits(kv, w, layer, which="k"):
+    """The GPU cache of one layer as bf16 bit patterns [B][H][Tb][hs]."""
+    t = kv.k if which == "k" else kv.v
+    a = t.cpu().numpy().view(np.uint16)
+    shp = (w.n_layer, kv.batch, w.n_head, w.block_size, w.n_embd // w.n_head)
+    return a[:int(np.prod(shp))].reshape(shp)[layer]
+
+
+def bf16_ulp_distance(bits, values):
+    """Distance in bf16 ulps between bf16 bit patterns and bf16-exact float
+    values (ordered-integer difference, so +0 and -0 are 1 apart at most)."""
+    vb = (np.asarray(values, np.float32).view(np.uint32) >> 16).astype(np.int64)
+    gb = np.asarray(bits).astype(np.int64)
+
+    def ordered(b):
+        return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+    return np.abs(ordered(gb) - ordered(vb))
 
 
 def make_model(w, weights, *, max_batch=None, max_prefill_tokens=None):
@@ -55,7 +82,8 @@ def dev_f64(a):
 
 
 def gpu_prefill(model, kv, ids, lens, limit=None):
-    model.prefill(kv, dev_i32(ids), list(lens), limit)
+    """Prefill through ngpt_prefill with host ids (checked by the library)."""
+    model.prefill(kv, np.ascontiguousarray(ids, dtype=np.int32), list(lens), limit)
     return model.logits(len(lens)).cpu().numpy().astype(np.float64)
 
 

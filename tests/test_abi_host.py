@@ -82,6 +82,23 @@ def test_config_validation(change, code):
     assert ng.kv_bytes(cfg, 1) == 0
 
 
+def test_workspace_bytes_covers_the_activation_buffers():
+    """The workspace holds at least the fp32 residual, the bf16 LayerNorm /
+    q / attention-output rows, the MLP activation and the fp32 logits of the
+    config's row bounds; it grows with max_prefill_tokens and max_batch, and
+    an invalid config gives 0."""
+    w = synth.workload("gpt2_124m_b1")
+    cfg = cfg_of(w, max_batch=1, max_prefill_tokens=1024)
+    n = ng.workspace_bytes(cfg)
+    C, V, M = 768, 50304, 1024
+    floor = M * C * 4 + 3 * M * C * 2 + M * 4 * C * 2 + V * 4
+    assert floor <= n < floor + (40 << 20)
+    assert ng.workspace_bytes(cfg_of(w, max_batch=1, max_prefill_tokens=2048)) > n
+    assert ng.workspace_bytes(cfg_of(w, max_batch=8, max_prefill_tokens=1024)) > n
+    assert ng.workspace_bytes(cfg_of(w, n_head=5)) == 0
+    assert n % 256 == 0
+
+
 def test_zero_layer_config_is_valid():
     w = synth.workload("char_4l128_fp32")
     assert ng.check_config(cfg_of(w, n_layer=0)) == ng.NGPT_OK
@@ -93,7 +110,7 @@ def test_create_rejects_bad_arguments_before_any_device_work():
     cfg = cfg_of(w)
     out = ctypes.c_void_p(1)
     # NULL weights
-    rc = lib.ngpt_create(ctypes.byref(cfg), None, None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(cfg), None, 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG and out.value is None
     # a bias pointer on a bias-free model
     layers = (ng.binding.LayerWeights * w.n_layer)()
@@ -101,16 +118,16 @@ def test_create_rejects_bad_arguments_before_any_device_work():
         for f in ng.binding._LAYER_FIELDS:
             setattr(layers[l], f, 0 if f.endswith("_b") else 4096)
     wt = ng.binding.Weights(4096, 4096, 4096, 4096, layers)
-    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG
     assert b"lnf_b" in lib.ngpt_last_error(None)
     # misaligned weight pointer
     wt = ng.binding.Weights(4096 + 2, 4096, 4096, 0, layers)
-    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG
     # misaligned lnf_w (the LayerNorm kernels read parameters 4 at a time)
     wt = ng.binding.Weights(4096, 4096, 4096 + 4, 0, layers)
-    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG and b"aligned" in lib.ngpt_last_error(None)
     # misaligned bias pointer on a model with biases
     bcfg = cfg_of(w, bias=1)
@@ -120,17 +137,27 @@ def test_create_rejects_bad_arguments_before_any_device_work():
             setattr(blayers[l], f, 4096)
     blayers[2].fc_b = 4096 + 8
     wt = ng.binding.Weights(4096, 4096, 4096, 4096, blayers)
-    rc = lib.ngpt_create(ctypes.byref(bcfg), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(bcfg), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG and b"aligned" in lib.ngpt_last_error(None)
     # missing layer weight
     layers[1].fc_w = 0
     wt = ng.binding.Weights(4096, 4096, 4096, 0, layers)
-    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_ARG
     # invalid config
     bad = cfg_of(w, n_head=3)
-    rc = lib.ngpt_create(ctypes.byref(bad), ctypes.byref(wt), None, ctypes.byref(out))
+    rc = lib.ngpt_create(ctypes.byref(bad), ctypes.byref(wt), 4096, 1 << 30, None, ctypes.byref(out))
     assert rc == ng.NGPT_E_CONFIG
+    # the caller-owned workspace: NULL, misaligned, too small
+    layers[1].fc_w = 4096
+    wt = ng.binding.Weights(4096, 4096, 4096, 0, layers)
+    need = ng.workspace_bytes(cfg)
+    for ws, nbytes, code in ((0, need, ng.NGPT_E_ARG), (4096 + 16, need, ng.NGPT_E_ARG),
+                             (4096, need - 1, ng.NGPT_E_SIZE)):
+        rc = lib.ngpt_create(ctypes.byref(cfg), ctypes.byref(wt), ws, nbytes, None,
+                             ctypes.byref(out))
+        assert rc == code and out.value is None, (ws, nbytes)
+        assert b"workspace" in lib.ngpt_last_error(None)
 
 
 def test_null_handle_calls_fail_cleanly():
@@ -138,6 +165,8 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.ngpt_destroy(None) == ng.NGPT_E_ARG
     assert lib.ngpt_set_sampling(None, 1.0, 0, 1) == ng.NGPT_E_ARG
     assert lib.ngpt_prefill(None, None, None, None, None, 1, 1) == ng.NGPT_E_ARG
+    assert lib.ngpt_prefill_device(None, None, None, None, None, 1, 1) == ng.NGPT_E_ARG
+    assert lib.ngpt_device_status(None, None) == ng.NGPT_E_ARG
     assert lib.ngpt_decode_step(None, None, None, None) == ng.NGPT_E_ARG
     assert lib.ngpt_decode_feed(None, None, None) == ng.NGPT_E_ARG
     assert lib.ngpt_sample(None, None, 1, 1, None, None) == ng.NGPT_E_ARG

@@ -139,7 +139,7 @@ def test_host_validation_errors():
     W = synth.make_weights(w)
     m = make_model(w, W, max_prefill_tokens=40)
     kv = m.new_kv(2)
-    ids = dev_i32(np.zeros((2, 32)))
+    ids = np.zeros((2, 32), np.int32)
     cases = [
         (([0, 5], None), ng.NGPT_E_RANGE),       # empty prompt
         (([33, 5], None), ng.NGPT_E_RANGE),      # longer than block_size
@@ -152,15 +152,30 @@ def test_host_validation_errors():
             m.prefill(kv, ids, lens, limit)
         assert ei.value.code == code, (lens, limit)
     with pytest.raises(ng.NgptError) as ei:      # B larger than the kv batch
-        m.prefill(kv, dev_i32(np.zeros((3, 4))), [4, 4, 4])
+        m.prefill(kv, np.zeros((3, 4), np.int32), [4, 4, 4])
     assert ei.value.code == ng.NGPT_E_ARG
+    for bad_id in (-1, w.vocab_size):            # host ids checked before the copy
+        bad = np.zeros((2, 32), np.int32)
+        bad[1, 3] = bad_id
+        with pytest.raises(ng.NgptError) as ei:
+            m.prefill(kv, bad, [5, 5])
+        assert ei.value.code == ng.NGPT_E_RANGE
+    bad = np.zeros((2, 32), np.int32)
+    bad[1, 7] = -5                               # past lens[1]: never read
+    m.prefill(kv, bad, [5, 5])
     m.set_sampling(temperature=1.0, top_k=0, greedy=False)
     m.prefill(kv, ids, [4, 4])
+    nxt = torch.empty(2, dtype=torch.int32, device="cuda")
     with pytest.raises(ng.NgptError) as ei:      # sampling needs uniforms
-        m.decode_step(kv, torch.empty(2, dtype=torch.int32, device="cuda"), None)
+        m.decode_step(kv, nxt, None)
     assert ei.value.code == ng.NGPT_E_ARG
     with pytest.raises(ng.NgptError):
         m.set_sampling(temperature=0.0, top_k=0, greedy=False)
+    other = m.new_kv(2)                          # not the cache of the last prefill
+    with pytest.raises(ng.NgptError) as ei:
+        m.decode_step(other, nxt, dev_f64([0.5, 0.5]))
+    assert ei.value.code == ng.NGPT_E_ARG
+    assert m.device_status() == ng.NGPT_OK
 
 
 def test_out_of_range_ids_are_reported_not_faulted():
@@ -169,6 +184,8 @@ def test_out_of_range_ids_are_reported_not_faulted():
     w = small("bf16", batch=1)
     m = make_model(w, synth.make_weights(w))
     kv = m.new_kv(1)
+    # device ids (ngpt_prefill_device) cannot be checked on the host: the
+    # kernel uses id 0 and raises the flag
     m.prefill(kv, dev_i32([[1, 2, w.vocab_size + 5, 3]]), [4])
     assert m.device_status() == ng.NGPT_E_DEVICE
     assert m.device_status() == ng.NGPT_OK       # cleared
@@ -279,6 +296,32 @@ def test_fused_greedy_step_matches_sampler_head_node():
         if s % 5 == 2 or s == 25:
             continue
         assert g_ids[s] == int(np.argmax(g_lg[s - 1]))
+
+
+def test_greedy_row_without_finite_maximum_same_rule_in_both_paths():
+    """A logits row with no finite maximum (here all NaN, from a NaN ln_f
+    gain) gives id 0 and the invalid-input flag, both from the sampler head
+    node (first step after a prefill) and from the one-launch kernel's own
+    greedy pick (later steps)."""
+    torch = need_gpu()
+    import gpt_decoder_amd as ng
+    w = small("bf16", L=2, H=4, C=256, Tb=64, V=300, bias=False, batch=1)
+    W = synth.make_weights(w)
+    W["lnf_w"] = np.full_like(W["lnf_w"], np.nan)
+    m = make_model(w, W)
+    m.set_sampling(greedy=True)
+    kv = m.new_kv(1)
+    gpu_prefill(m, kv, np.arange(8, dtype=np.int32)[None], [8])
+    assert np.isnan(m.logits(1).cpu().numpy()).all()
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    got = []
+    for s in range(4):
+        m.decode_step(kv, nxt, None)
+        got.append(int(nxt.item()))
+        assert m.device_status() == ng.NGPT_E_DEVICE, s
+    assert got == [0, 0, 0, 0]
+    assert kv.lens.cpu().tolist() == [12]
+    m.close()
 
 
 @pytest.mark.parametrize("L,H,C,Tb,plen,steps,bias", [

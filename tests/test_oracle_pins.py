@@ -212,26 +212,46 @@ def test_attention_mask_matches_page_diagram():
 # A second, independent model built from torch modules (third opinion)
 # --------------------------------------------------------------------------
 
-def torch_reference_logits(cfg, w, ids):
+BF16_POINTS = ("h1", "q", "k", "v", "y", "h2", "f", "z")
+
+
+def torch_bf16(a):
+    """Round a float64 tensor through torch's own float32 and bfloat16
+    conversions (round to nearest even), back to float64."""
+    return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def torch_reference_logits(cfg, w, ids, cast_points=()):
     """All-position logits of one sequence, written with torch.nn.functional
     from the page fragments: embedding sum, pre-LN blocks with SDPA
-    (is_causal=True), exact GELU, tied bias-free head."""
+    (is_causal=True), exact GELU, tied bias-free head.
+
+    ``cast_points`` names the tensors that are rounded to bfloat16 with
+    torch's conversion where a bf16 data path stores them: the two
+    LayerNorm outputs of a block (h1, h2), q, k, v, the attention output y,
+    the GELU output f and the final LayerNorm output z.  "x" (the residual
+    stream after each add, which a bf16 data path keeps in fp32) exists only
+    to show that rounding it is detected.
+    """
     t = lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float64))
+    cp = set(cast_points)
+    r = lambda name, a: torch_bf16(a) if name in cp else a
     C, H = cfg.n_embd, cfg.n_head
     ids_t = torch.as_tensor(np.asarray(ids), dtype=torch.long)
     T = len(ids)
     x = F.embedding(ids_t, t(w["wte"])) + F.embedding(torch.arange(T), t(w["wpe"]))
     for lw in w["layers"]:
-        h = F.layer_norm(x, (C,), t(lw["ln1_w"]), t(lw["ln1_b"]), 1e-5)
+        h = r("h1", F.layer_norm(x, (C,), t(lw["ln1_w"]), t(lw["ln1_b"]), 1e-5))
         q, k, v = F.linear(h, t(lw["attn_w"]), t(lw["attn_b"])).split(C, dim=1)
-        q, k, v = (a.view(T, H, C // H).transpose(0, 1) for a in (q, k, v))
+        q, k, v = r("q", q), r("k", k), r("v", v)
+        q, k, v = (a.reshape(T, H, C // H).transpose(0, 1) for a in (q, k, v))
         y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
-        y = y.transpose(0, 1).reshape(T, C)
-        x = x + F.linear(y, t(lw["attnproj_w"]), t(lw["attnproj_b"]))
-        h = F.layer_norm(x, (C,), t(lw["ln2_w"]), t(lw["ln2_b"]), 1e-5)
-        f = F.gelu(F.linear(h, t(lw["fc_w"]), t(lw["fc_b"])))
-        x = x + F.linear(f, t(lw["mlpproj_w"]), t(lw["mlpproj_b"]))
-    z = F.layer_norm(x, (C,), t(w["lnf_w"]), t(w["lnf_b"]), 1e-5)
+        y = r("y", y.transpose(0, 1).reshape(T, C))
+        x = r("x", x + F.linear(y, t(lw["attnproj_w"]), t(lw["attnproj_b"])))
+        h = r("h2", F.layer_norm(x, (C,), t(lw["ln2_w"]), t(lw["ln2_b"]), 1e-5))
+        f = r("f", F.gelu(F.linear(h, t(lw["fc_w"]), t(lw["fc_b"]))))
+        x = r("x", x + F.linear(f, t(lw["mlpproj_w"]), t(lw["mlpproj_b"])))
+    z = r("z", F.layer_norm(x, (C,), t(w["lnf_w"]), t(w["lnf_b"]), 1e-5))
     return F.linear(z, t(w["wte"])).numpy()
 
 
@@ -364,6 +384,33 @@ def test_bf16_mode_rounds_cache_and_stays_close():
     assert 0 < err < 2e-2
 
 
+@pytest.mark.parametrize("bias,gamma", [(False, 0.0), (True, 0.1)])
+def test_bf16_mode_matches_torch_model_with_bf16_casts(bias, gamma):
+    """The bf16 mode equals an independent torch model that rounds h1, q,
+    k, v, y, h2, f and z through torch.bfloat16 and nothing else (3 blocks,
+    with and without biases, every position)."""
+    cfg = small_cfg(L=3, bias=bias)
+    w = synth.make_weights(cfg, gamma_std=gamma)
+    ids = rng.integers(0, cfg.vocab_size, 24)
+    mine = OracleGPT(cfg, w, act_bf16=True).full_logits(ids, positions=list(range(24)))
+    want = torch_reference_logits(cfg, w, ids, cast_points=BF16_POINTS)
+    np.testing.assert_allclose(mine, want, rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("dropped", BF16_POINTS + ("+x",))
+def test_bf16_pin_detects_each_rounding_point(dropped):
+    """The comparison above is sensitive to every rounding point: the torch
+    model without any one of them (or with the residual stream rounded too)
+    misses the bf16 mode by far more than the 1e-9 bar."""
+    cfg = small_cfg(L=3, bias=True)
+    w = synth.make_weights(cfg, gamma_std=0.1)
+    ids = rng.integers(0, cfg.vocab_size, 24)
+    mine = OracleGPT(cfg, w, act_bf16=True).full_logits(ids, positions=list(range(24)))
+    pts = [p for p in BF16_POINTS if p != dropped] + (["x"] if dropped == "+x" else [])
+    other = torch_reference_logits(cfg, w, ids, cast_points=pts)
+    assert np.max(np.abs(mine - other)) > 1e-6
+
+
 # --------------------------------------------------------------------------
 # Parameter count (model-building chapter, sections 4.3 and 4.5)
 # --------------------------------------------------------------------------
@@ -415,16 +462,18 @@ def test_topk_one_keeps_the_maxima():
     assert list(np.nonzero(topk_keep_set(s, 1))[0]) == [1, 3]
 
 
-def test_sampler_matches_page_procedure_probabilities():
-    """Sweeping u over a fine grid reproduces the probabilities of the
-    page's procedure (divide, mask below the k-th value with -inf, softmax),
-    computed here with torch."""
+def test_sampler_matches_definition_probabilities():
+    """Sweeping u over a fine grid reproduces the probabilities the
+    definition gives: scaled logits s = l / T, the kept set = values not
+    below the k-th largest (found here by a full descending sort),
+    probability exp(s_i - max) normalised over the kept set, zero outside."""
     V, k, T = 12, 5, 0.8
     lg = rng.standard_normal(V).astype(np.float32) * 2
-    t = torch.from_numpy(lg.astype(np.float64)) / T
-    v, _ = torch.topk(t, min(k, V))
-    t[t < v[-1]] = -float("inf")
-    p = torch.softmax(t, -1).numpy()
+    s = lg.astype(np.float64) / T
+    kth = sorted(s.tolist(), reverse=True)[min(k, V) - 1]
+    kept = np.array([x >= kth for x in s.tolist()])
+    e = np.where(kept, np.exp(s - s.max()), 0.0)
+    p = e / e.sum()
     N = 200000
     counts = np.zeros(V)
     for i in range(N):
