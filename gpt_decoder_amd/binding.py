@@ -171,7 +171,7 @@ class Model:
 
     def __init__(self, *, n_layer, n_head, n_embd, block_size, vocab_size,
                  bias, dtype, weights, max_batch, max_prefill_tokens,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, static_workspace=False):
         import torch
         self.torch = torch
         self.device = torch.device(device)
@@ -202,18 +202,28 @@ class Model:
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         self.stream = stream
-        # caller-owned workspace (torch's allocations are 256-byte aligned)
-        nws = workspace_bytes(self.cfg)
-        if nws == 0:
-            raise NgptError(NGPT_E_CONFIG, "invalid config")
-        self.workspace = torch.empty(nws, dtype=torch.uint8, device=self.device)
         self._status = torch.zeros(1, dtype=torch.int32, device=self.device)
         h = ctypes.c_void_p()
-        rc = lib().ngpt_create(ctypes.byref(self.cfg),
-                               ctypes.byref(self._weights),
-                               _ptr(self.workspace), nws,
-                               ctypes.c_void_p(stream.cuda_stream),
-                               ctypes.byref(h))
+        if static_workspace:
+            # the library's fixed per-device workspace: no allocation at all
+            self.workspace = None
+            fn = lib().ngpt_create_static
+            fn.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                           ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+            fn.restype = ctypes.c_int
+            rc = fn(ctypes.byref(self.cfg), ctypes.byref(self._weights),
+                    ctypes.c_void_p(stream.cuda_stream), ctypes.byref(h))
+        else:
+            # caller-owned workspace (torch's allocations are 256-byte aligned)
+            nws = workspace_bytes(self.cfg)
+            if nws == 0:
+                raise NgptError(NGPT_E_CONFIG, "invalid config")
+            self.workspace = torch.empty(nws, dtype=torch.uint8, device=self.device)
+            rc = lib().ngpt_create(ctypes.byref(self.cfg),
+                                   ctypes.byref(self._weights),
+                                   _ptr(self.workspace), nws,
+                                   ctypes.c_void_p(stream.cuda_stream),
+                                   ctypes.byref(h))
         if rc != NGPT_OK:
             raise NgptError(rc, lib().ngpt_last_error(None).decode())
         self.h = h
@@ -312,7 +322,7 @@ class Model:
 
 
 def model_from_workload(w, weights, *, max_batch=None, max_prefill_tokens=None,
-                        device="cuda", stream=None) -> Model:
+                        device="cuda", stream=None, static_workspace=False) -> Model:
     """Model for a ``synth.Workload``-like shape description."""
     mb = max_batch or w.batch
     mpt = max_prefill_tokens or mb * w.block_size
@@ -320,4 +330,5 @@ def model_from_workload(w, weights, *, max_batch=None, max_prefill_tokens=None,
                  n_embd=w.n_embd, block_size=w.block_size,
                  vocab_size=w.vocab_size, bias=weights["lnf_b"] is not None,
                  dtype=w.dtype, weights=weights, max_batch=mb,
-                 max_prefill_tokens=mpt, device=device, stream=stream)
+                 max_prefill_tokens=mpt, device=device, stream=stream,
+                 static_workspace=static_workspace)

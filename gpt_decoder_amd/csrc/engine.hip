@@ -15,6 +15,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -112,6 +114,19 @@ const char* status_name(int s) {
 
 std::string g_static_error;
 
+// The workspace of ngpt_create_static(): a fixed array of the library, one
+// copy per GPU at that GPU's own address.  Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress
+// (taken once per device, with the device current) and is what the kernels
+// receive.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+struct StaticSlot {
+  void* ptr = nullptr;   // device address of `scratch` on this device
+  bool live = false;     // a model currently uses it
+};
+std::mutex g_static_mu;
+std::map<int, StaticSlot> g_static_slots;
+
 }  // namespace
 
 // Byte offsets of the workspace regions (every region 256-byte aligned).
@@ -123,6 +138,8 @@ struct WsLayout {
   size_t eq, er, ey, e1, ef, e2, epoch, ecand, dlayers;
   size_t total = 0;
 };
+
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
 
 struct ngpt_model {
   ngpt_config cfg{};
@@ -165,6 +182,7 @@ struct ngpt_model {
   // the KV cache of the last prefill and the host record of its lengths
   ngpt_kv rec_kv{};
   std::vector<int32_t> h_lens, h_limit;
+  int static_dev = -1;          // device whose static workspace this model uses
   GraphSlot g_step, g_feed;
   std::string err;
 };
@@ -397,6 +415,10 @@ static void drop_graph(GraphSlot& g) {
 
 static int release(ngpt_model* m) {
   hipError_t e = hipStreamSynchronize(m->stream);
+  if (m->static_dev >= 0) {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    g_static_slots[m->static_dev].live = false;
+  }
   drop_graph(m->g_step);
   drop_graph(m->g_feed);
   if (m->cap) (void)hipStreamDestroy(m->cap);
@@ -426,6 +448,38 @@ int ngpt_create(const ngpt_config* cfg, const ngpt_weights* w, void* workspace,
   rc = check_weights(cfg, w);
   if (rc != NGPT_OK) return rc;
   return create_on(cfg, w, workspace, ws_bytes, stream, out);
+}
+
+int ngpt_create_static(const ngpt_config* cfg, const ngpt_weights* w, void* stream,
+                       ngpt_model** out) {
+  if (!out) return fail(nullptr, NGPT_E_ARG, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  int rc = check_config(cfg, &why);
+  if (rc != NGPT_OK) return fail(nullptr, rc, why);
+  rc = check_weights(cfg, w);
+  if (rc != NGPT_OK) return rc;
+  if (ws_layout(cfg).total > kStaticWorkspaceBytes)
+    return fail(nullptr, NGPT_E_SIZE, "config needs more workspace than the static array holds");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(nullptr, NGPT_E_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  StaticSlot& slot = g_static_slots[dev];
+  if (slot.live)
+    return fail(nullptr, NGPT_E_ARG, "a model already uses this device's static workspace");
+  if (!slot.ptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, NGPT_E_HIP, std::string("hipGetSymbolAddress(static workspace): ") +
+                                           hipGetErrorString(e));
+    slot.ptr = p;
+  }
+  rc = create_on(cfg, w, slot.ptr, kStaticWorkspaceBytes, stream, out);
+  if (rc != NGPT_OK) return rc;
+  (*out)->static_dev = dev;
+  slot.live = true;
+  return NGPT_OK;
 }
 
 int ngpt_destroy(ngpt_model* m) {

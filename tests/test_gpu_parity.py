@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (TOL_BF16, TOL_F32, Timer, bf16_ulp_distance, dev_f64,
+from gpu_common import (TOL_BF16, TOL_F32, Timer, bf16_ulp_distance, check_cache_stage, dev_f64,
                         dev_i32, gpu_prefill, kv_layer_bits, log, make_exact_oracle,
                         make_model, make_oracle, max_abs, need_gpu, tol_for)
 
@@ -203,24 +203,21 @@ def test_gpt2_124m_prefill_1024():
     assert e < TOL_BF16
     assert ex < TOL_BF16
     # stage check: layer 0's K and V (LN1 of the embeddings through c_attn
-    # and the q/k/v epilogue into the cache) match the oracle's bf16 cache
-    # at every position, head and dimension within one bf16 ulp of the
-    # oracle value, or 1e-3 absolute for values near zero (a LayerNorm
-    # output that rounds the other way at a tie moves a K entry by up to
-    # ~1e-3; a wrong row, head or position moves it by ~|K| ~ 0.5); the
-    # last layer's cache is reported
+    # and the q/k/v epilogue into the cache) against the oracle's bf16 cache
+    # at every position, head and dimension (criterion in check_cache_stage);
+    # the last layer's cache is reported
     hs = w.n_embd // w.n_head
     for layer in (0, w.n_layer - 1):
         for which in ("k", "v"):
             bits = kv_layer_bits(kv, w, layer, which)[0][:, :1024]   # [H][T][hs]
             ref_c = (o.caches[0].k if which == "k" else o.caches[0].v)[layer]
             want = ref_c.reshape(1024, w.n_head, hs).transpose(1, 0, 2)
-            gotv = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            d = bf16_ulp_distance(bits, want)
-            err = np.abs(gotv - want)
-            ok = (d <= 1) | (err <= 1e-3)
-            log(f"  layer {layer} {which}: {float((d > 1).mean()):.2e} of entries "
-                f"above 1 ulp, max abs diff {err.max():.2e}")
             if layer == 0:
-                assert ok.all()
+                frac, err = check_cache_stage(bits, want)
+            else:
+                gv = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                frac = float((bf16_ulp_distance(bits, want) > 1).mean())
+                err = float(np.abs(gv - want).max())
+            log(f"  layer {layer} {which}: {frac:.2e} of entries beyond one ulp, "
+                f"max abs diff {err:.2e}")
     m.close()

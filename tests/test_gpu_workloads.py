@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (TOL_BF16, Timer, bf16_ulp_distance, dev_f64, dev_i32,
+from gpu_common import (TOL_BF16, Timer, check_cache_stage, dev_f64, dev_i32,
                         draws_must_agree, gpu_prefill, greedy_must_agree,
                         kv_layer_bits, log, make_exact_oracle, make_model,
                         make_oracle, max_abs, need_gpu)
@@ -157,7 +157,7 @@ def test_gpt2_124m_bias_ragged_batch64_full():
     lw = W["layers"][0]
     kb, vb = kv_layer_bits(kv, w, 0, "k"), kv_layer_bits(kv, w, 0, "v")
     C, hs = w.n_embd, w.n_embd // w.n_head
-    worst = 0
+    worst, fr_max = 0.0, 0.0
     for b in range(w.batch):
         L0 = int(lens[b])
         x0 = W["wte"][ids[b, :L0]].astype(np.float64) + W["wpe"][:L0]
@@ -166,12 +166,11 @@ def test_gpt2_124m_bias_ragged_batch64_full():
         for which, bits in (("k", kb), ("v", vb)):
             off = C if which == "k" else 2 * C
             want = oracle.round_bf16(qkv[:, off:off + C]).reshape(L0, w.n_head, hs).transpose(1, 0, 2)
-            gb = bits[b][:, :L0]
-            gv = (gb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            d = bf16_ulp_distance(gb, want)
-            assert ((d <= 1) | (np.abs(gv - want) <= 1e-3)).all(), (b, which)
-            worst = max(worst, int(d.max()))
-    log(f"  layer-0 K/V of all {w.batch} rows match (largest ulp distance {worst})")
+            frac, err = check_cache_stage(bits[b][:, :L0], want)
+            worst = max(worst, err)
+            fr_max = max(fr_max, frac)
+    log(f"  layer-0 K/V of all {w.batch} rows match: largest abs diff {worst:.2e}, "
+        f"at most {fr_max:.2e} of a row's entries beyond one ulp")
     want_steps = {b: {0, 1, 100, 1024 - int(lens[b]) - 1} for b in rows}
     caught = {b: {} for b in rows}
     for s in range(steps):
