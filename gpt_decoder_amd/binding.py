@@ -92,6 +92,12 @@ def lib():
     L.ngpt_prefill_device.argtypes = [vp, ctypes.POINTER(KV), vp,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32),
                                       i32, i32]
+    L.ngpt_prefill_slots.argtypes = [vp, ctypes.POINTER(KV), vp, vp,
+                                     ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     i32, i32]
+    L.ngpt_extend.argtypes = [vp, ctypes.POINTER(KV), vp, vp, vp, i32, i32]
+    L.ngpt_retire.argtypes = [vp, ctypes.POINTER(KV), vp, i32]
+    L.ngpt_slide.argtypes = [vp, ctypes.POINTER(KV), vp, i32, vp]
     L.ngpt_decode_step.argtypes = [vp, ctypes.POINTER(KV), vp, vp]
     L.ngpt_decode_feed.argtypes = [vp, ctypes.POINTER(KV), vp]
     L.ngpt_sample.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -105,6 +111,7 @@ def lib():
     L.ngpt_status_string.restype = ctypes.c_char_p
     for name in ("ngpt_check_config", "ngpt_create", "ngpt_destroy",
                  "ngpt_set_sampling", "ngpt_prefill", "ngpt_prefill_device",
+                 "ngpt_prefill_slots", "ngpt_extend", "ngpt_retire", "ngpt_slide",
                  "ngpt_decode_step",
                  "ngpt_decode_feed", "ngpt_sample", "ngpt_logits",
                  "ngpt_copy_logits", "ngpt_device_status", "ngpt_set_wait_limit"):
@@ -259,6 +266,45 @@ class Model:
         self._check(lib().ngpt_prefill(
             self.h, ctypes.byref(kv.struct),
             a.ctypes.data_as(ctypes.c_void_p), lens_a, lim_a, B, Tmax))
+
+    @staticmethod
+    def _host_i32(a):
+        return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+    def prefill_slots(self, kv: KVCache, slots, ids, lens, limit=None):
+        """Admit prompts (host ids [n, Tmax]) into kv rows ``slots``."""
+        sl = self._host_i32(slots)
+        a = self._host_i32(ids)
+        n, Tmax = a.shape
+        lens_a = (ctypes.c_int32 * n)(*[int(x) for x in lens])
+        lim_a = None if limit is None else (ctypes.c_int32 * n)(
+            *[int(x) for x in limit])
+        self._check(lib().ngpt_prefill_slots(
+            self.h, ctypes.byref(kv.struct), sl.ctypes.data_as(ctypes.c_void_p),
+            a.ctypes.data_as(ctypes.c_void_p), lens_a, lim_a, n, Tmax))
+
+    def extend(self, kv: KVCache, slots, ids, counts):
+        """Append counts[b] tokens (host ids [n, Tmax]) to live rows."""
+        sl, a, c = self._host_i32(slots), self._host_i32(ids), self._host_i32(counts)
+        n, Tmax = a.shape
+        self._check(lib().ngpt_extend(
+            self.h, ctypes.byref(kv.struct), sl.ctypes.data_as(ctypes.c_void_p),
+            a.ctypes.data_as(ctypes.c_void_p), c.ctypes.data_as(ctypes.c_void_p),
+            n, Tmax))
+
+    def retire(self, kv: KVCache, slots):
+        sl = self._host_i32(slots)
+        self._check(lib().ngpt_retire(self.h, ctypes.byref(kv.struct),
+                                      sl.ctypes.data_as(ctypes.c_void_p), len(sl)))
+
+    def slide(self, kv: KVCache, slots, next_ids):
+        """Crop full rows to their last block_size - 1 tokens plus
+        next_ids[row] (device int32 [batch]) and run that window."""
+        sl = self._host_i32(slots)
+        assert next_ids.dtype == self.torch.int32 and next_ids.is_cuda
+        self._check(lib().ngpt_slide(self.h, ctypes.byref(kv.struct),
+                                     sl.ctypes.data_as(ctypes.c_void_p), len(sl),
+                                     _ptr(next_ids)))
 
     def decode_step(self, kv: KVCache, next_ids, uniforms):
         """``next_ids``: device int32 [batch] (out); ``uniforms``: device

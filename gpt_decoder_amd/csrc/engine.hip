@@ -27,8 +27,9 @@ using namespace ngpt;
 
 namespace {
 
+// New lens / limit of the rows of a kv batch; -1 leaves a value unchanged.
 struct LensArgs {
-  int32_t n;        // rows of the kv batch to set
+  int32_t n;        // rows of the kv batch
   int32_t lens[NGPT_MAX_BATCH];
   int32_t limit[NGPT_MAX_BATCH];
 };
@@ -36,9 +37,24 @@ struct LensArgs {
 __global__ void set_lens_kernel(LensArgs a, int32_t* lens, int32_t* limit) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < a.n) {
-    lens[b] = a.lens[b];
-    limit[b] = a.limit[b];
+    if (a.lens[b] >= 0) lens[b] = a.lens[b];
+    if (a.limit[b] >= 0) limit[b] = a.limit[b];
   }
+}
+
+// Ids of a cropped window (generate() beyond block_size): for each listed
+// row, its cached tokens 1 .. Tb-1 (from the token history) followed by the
+// row's new token; packed, Tb ids per row.
+struct SlotList {
+  int32_t n;
+  int32_t slot[NGPT_MAX_BATCH];
+};
+__global__ void window_ids_kernel(SlotList sl, const int32_t* hist, int Tb,
+                                  const int32_t* next, int32_t* out) {
+  const int i = blockIdx.y, p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= sl.n || p >= Tb) return;
+  const int b = sl.slot[i];
+  out[(size_t)i * Tb + p] = p + 1 < Tb ? hist[(size_t)b * Tb + p + 1] : next[b];
 }
 
 // Report and clear the kernel-side flags: bit 2 a one-launch decode wait
@@ -131,8 +147,8 @@ std::map<int, StaticSlot> g_static_slots;
 
 // Byte offsets of the workspace regions (every region 256-byte aligned).
 struct WsLayout {
-  size_t x, h, q, y, f, z, logits, row_b, row_pos, last_rows, part, ppart, ids,
-      tok, pos, status, params, done;
+  size_t x, h, q, y, f, z, logits, row_b, row_pos, last_rows, last_slot, hist,
+      part, ppart, ids, tok, pos, status, params, done;
   // one-launch decode exchange buffers (absent: persist_shape == false)
   bool persist_shape = false;
   size_t eq, er, ey, e1, ef, e2, epoch, ecand, dlayers;
@@ -156,6 +172,8 @@ struct ngpt_model {
   void *h = nullptr, *q = nullptr, *y = nullptr, *f = nullptr, *z = nullptr;
   float* logits = nullptr;
   int32_t *row_b = nullptr, *row_pos = nullptr, *last_rows = nullptr;
+  int32_t* last_slot = nullptr;  // cache row of each prefilled sequence
+  int32_t* hist = nullptr;       // token history [max_batch][Tb]
   float* part = nullptr;
   float* ppart = nullptr;   // prefill attention key-split partials (one sequence)
   int32_t* d_ids = nullptr; // packed prompt ids copied from the host
@@ -272,6 +290,7 @@ static WsLayout ws_layout(const ngpt_config* cfg) {
   o.y = carve(Mm * C * es); o.f = carve(Mm * 4 * C * es); o.z = carve(Bm * C * es);
   o.logits = carve(Bm * (size_t)cfg->vocab_size * 4);
   o.row_b = carve(Mm * 4); o.row_pos = carve(Mm * 4); o.last_rows = carve(Bm * 4);
+  o.last_slot = carve(Bm * 4); o.hist = carve(Bm * (size_t)Tb * 4);
   o.part = carve(Bm * H * (size_t)nchunk * (hs + 2) * 4);
   o.ppart = carve((size_t)H * Tb * attn_prefill_split_chunks(Tb) * (hs + 4) * 4);
   o.ids = carve((size_t)cfg->max_prefill_tokens * 4);
@@ -353,6 +372,7 @@ static int create_on(const ngpt_config* cfg, const ngpt_weights* w, void* ws,
   m->logits = (float*)(base + o.logits);
   m->row_b = (int32_t*)(base + o.row_b); m->row_pos = (int32_t*)(base + o.row_pos);
   m->last_rows = (int32_t*)(base + o.last_rows); m->part = (float*)(base + o.part);
+  m->last_slot = (int32_t*)(base + o.last_slot); m->hist = (int32_t*)(base + o.hist);
   m->ppart = (float*)(base + o.ppart);
   m->d_ids = (int32_t*)(base + o.ids);
   m->tok = (int32_t*)(base + o.tok);
@@ -531,48 +551,140 @@ static void* layer_cache(const ngpt_model* m, void* base, int l, int kvB) {
          (size_t)l * kvB * m->H * m->Tb * m->hs * m->esz;
 }
 
-// Host checks shared by both prefill entry points; fills the row map and
-// the lens/limit record.
-static int plan_prefill(ngpt_model* m, const ngpt_kv* kv, const int32_t* lens,
-                        const int32_t* limit, int32_t B, int32_t Tmax, RowMap& map,
-                        LensArgs& la, int& maxlen) {
+// Which rows a launch of the prefill sequence processes, and how the host
+// record and the device lens / limit change.
+struct RowPlan {
+  RowMap map{};
+  LensArgs la{};
+  int maxlen = 0;        // most new rows of one sequence
+  bool reset = false;    // the kv becomes the recorded cache; other rows inactive
+};
+
+// Prompts of B sequences into kv rows `slots` (NULL: 0 .. B-1) from an empty
+// cache.  With reset, every other row of the kv becomes inactive.
+static int plan_prompts(ngpt_model* m, const ngpt_kv* kv, const int32_t* slots,
+                        const int32_t* lens, const int32_t* limit, int32_t B,
+                        int32_t Tmax, bool reset, RowPlan& pl) {
   int rc = check_kv(m, kv);
   if (rc != NGPT_OK) return rc;
   if (!lens) return fail(m, NGPT_E_ARG, "lens is NULL");
   if (B < 1 || B > kv->batch) return fail(m, NGPT_E_ARG, "B must be in [1, kv->batch]");
-  map.B = B;
-  la.n = kv->batch;
+  pl.map.B = B;
+  pl.la.n = kv->batch;
+  pl.reset = reset;
+  for (int b = 0; b < kv->batch; ++b) {
+    pl.la.lens[b] = reset ? 0 : -1;
+    pl.la.limit[b] = reset ? 0 : -1;
+  }
+  std::vector<char> seen(kv->batch, 0);
   long total = 0;
-  maxlen = 0;
   for (int b = 0; b < B; ++b) {
+    const int sl = slots ? slots[b] : b;
+    if (sl < 0 || sl >= kv->batch) return fail(m, NGPT_E_RANGE, "slot outside [0, kv->batch)");
+    if (seen[sl]) return fail(m, NGPT_E_ARG, "a slot is listed twice");
+    seen[sl] = 1;
     const int lb = lens[b];
     const int lim = limit ? limit[b] : m->Tb;
     if (lb < 1 || lb > m->Tb) return fail(m, NGPT_E_RANGE, "lens[b] must be in [1, block_size]");
     if (lim < lb || lim > m->Tb) return fail(m, NGPT_E_RANGE, "limit[b] must be in [lens[b], block_size]");
     if (lb > Tmax) return fail(m, NGPT_E_ARG, "lens[b] > Tmax");
-    map.off[b] = (int32_t)total;
+    pl.map.off[b] = (int32_t)total;
+    pl.map.slot[b] = sl;
+    pl.map.past[b] = 0;
     total += lb;
-    maxlen = std::max(maxlen, lb);
-    la.lens[b] = lb;
-    la.limit[b] = lim;
+    pl.maxlen = std::max(pl.maxlen, lb);
+    pl.la.lens[sl] = lb;
+    pl.la.limit[sl] = lim;
   }
-  map.off[B] = (int32_t)total;
+  pl.map.off[B] = (int32_t)total;
   if (total > m->cfg.max_prefill_tokens)
     return fail(m, NGPT_E_SIZE, "sum(lens) > max_prefill_tokens");
-  for (int b = B; b < kv->batch; ++b) { la.lens[b] = 0; la.limit[b] = 0; }
   return NGPT_OK;
 }
 
-// The prefill launch sequence.  ids: device; Tmax > 0 gives the [B][Tmax]
-// right-padded layout, Tmax == 0 the packed layout (row r of the map).
-static int enqueue_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
-                           const RowMap& map, const LensArgs& la, int maxlen) {
+// counts[b] new tokens appended to live rows slots[b] of the recorded cache.
+static int plan_extend(ngpt_model* m, const ngpt_kv* kv, const int32_t* slots,
+                       const int32_t* counts, int32_t n, int32_t Tmax, RowPlan& pl) {
+  int rc = check_kv(m, kv);
+  if (rc != NGPT_OK) return rc;
+  if (m->h_lens.empty() || !same_kv(*kv, m->rec_kv))
+    return fail(m, NGPT_E_ARG, "kv is not the cache of the last prefill on this model");
+  if (!slots || !counts) return fail(m, NGPT_E_ARG, "slots or counts is NULL");
+  if (n < 1 || n > kv->batch) return fail(m, NGPT_E_ARG, "n must be in [1, kv->batch]");
+  pl.map.B = n;
+  pl.la.n = kv->batch;
+  for (int b = 0; b < kv->batch; ++b) pl.la.lens[b] = pl.la.limit[b] = -1;
+  std::vector<char> seen(kv->batch, 0);
+  long total = 0;
+  for (int b = 0; b < n; ++b) {
+    const int sl = slots[b];
+    if (sl < 0 || sl >= kv->batch) return fail(m, NGPT_E_RANGE, "slot outside [0, kv->batch)");
+    if (seen[sl]) return fail(m, NGPT_E_ARG, "a slot is listed twice");
+    seen[sl] = 1;
+    const int c = counts[b];
+    if (c < 1 || c > Tmax) return fail(m, NGPT_E_RANGE, "counts[b] must be in [1, Tmax]");
+    if (m->h_lens[sl] + c > m->h_limit[sl])
+      return fail(m, NGPT_E_CONTEXT, "the row cannot take that many tokens (limit)");
+    pl.map.off[b] = (int32_t)total;
+    pl.map.slot[b] = sl;
+    pl.map.past[b] = m->h_lens[sl];
+    total += c;
+    pl.maxlen = std::max(pl.maxlen, c);
+    pl.la.lens[sl] = m->h_lens[sl] + c;
+  }
+  pl.map.off[n] = (int32_t)total;
+  if (total > m->cfg.max_prefill_tokens)
+    return fail(m, NGPT_E_SIZE, "sum(counts) > max_prefill_tokens");
+  return NGPT_OK;
+}
+
+// Every id of the plan's sequences on the host, then a packed asynchronous
+// copy through the pinned staging into the workspace.
+static int stage_host_ids(ngpt_model* m, const RowPlan& pl, const int32_t* ids, int Tmax) {
+  const RowMap& map = pl.map;
+  for (int b = 0; b < map.B; ++b) {
+    const int cnt = map.off[b + 1] - map.off[b];
+    for (int p = 0; p < cnt; ++p) {
+      const int32_t id = ids[(size_t)b * Tmax + p];
+      if (id < 0 || id >= m->V)
+        return fail(m, NGPT_E_RANGE, "token id outside [0, vocab_size)");
+    }
+  }
+  const size_t half = (size_t)m->cfg.max_prefill_tokens;
+  if (!m->pinned) {
+    HIP_TRY(m, hipHostMalloc(reinterpret_cast<void**>(&m->pinned), 2 * half * sizeof(int32_t),
+                             hipHostMallocDefault));
+    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[0], hipEventDisableTiming));
+    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[1], hipEventDisableTiming));
+  }
+  const int hf = m->pinned_half;
+  if (m->pinned_used[hf]) HIP_TRY(m, hipEventSynchronize(m->pinned_ev[hf]));
+  int32_t* stage = m->pinned + hf * half;
+  for (int b = 0; b < map.B; ++b)
+    memcpy(stage + map.off[b], ids + (size_t)b * Tmax,
+           sizeof(int32_t) * (map.off[b + 1] - map.off[b]));
+  const int M = map.off[map.B];
+  HIP_TRY(m, hipMemcpyAsync(m->d_ids, stage, sizeof(int32_t) * M, hipMemcpyHostToDevice,
+                            m->stream));
+  HIP_TRY(m, hipEventRecord(m->pinned_ev[hf], m->stream));
+  m->pinned_used[hf] = true;
+  m->pinned_half = hf ^ 1;
+  return NGPT_OK;
+}
+
+// The prefill launch sequence over the plan's rows.  ids: device; Tmax > 0
+// gives the [B][Tmax] right-padded layout, Tmax == 0 the packed layout.
+// Leaves the logits of each sequence's last new row in its slot's row.
+static int enqueue_rows(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
+                        const RowPlan& pl) {
+  const RowMap& map = pl.map;
   const int M = map.off[map.B], C = m->C, dt = m->cfg.dtype, B = map.B;
   hipStream_t s = m->stream;
   m->cand_ok = false;   // the logits are about to come from this prefill
-  set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(la, kv->lens, kv->limit);
+  set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(pl.la, kv->lens, kv->limit);
   launch_embed_prefill(dt, ids, Tmax, map, M, m->wte, m->wpe, C, m->V, m->x,
-                       m->row_b, m->row_pos, m->last_rows, m->status, s);
+                       m->row_b, m->row_pos, m->last_rows, m->last_slot, m->hist,
+                       m->Tb, m->status, s);
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, kv->batch);
@@ -583,7 +695,7 @@ static int enqueue_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int T
     eq.row_b = m->row_b; eq.row_pos = m->row_pos;
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
     launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, M, 3 * C, C, eq, s);
-    launch_attn_prefill(dt, m->q, C, kl, vl, map, maxlen, m->H, m->hs, m->Tb,
+    launch_attn_prefill(dt, m->q, C, kl, vl, map, pl.maxlen, m->H, m->hs, m->Tb,
                         m->y, C, m->ppart, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
@@ -596,18 +708,24 @@ static int enqueue_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int T
     em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
     launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, M, C, 4 * C, em, s);
   }
-  // ln_f and the tied lm_head on each sequence's last row only
+  // ln_f and the tied lm_head on each sequence's last row only, into the
+  // logits row of its slot
   launch_layernorm(dt, m->x, C, m->last_rows, B, m->lnf_w, m->lnf_b, m->z, C, C, s);
   EpiArgs el;
-  el.out = m->logits; el.ldo = m->V;
+  el.out = m->logits; el.ldo = m->V; el.row_b = m->last_slot;
   launch_linear(dt, EPI_LOGITS, m->z, C, nullptr, m->wte, B, m->V, C, el, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
 
-  m->rec_kv = *kv;
-  m->h_lens.assign(kv->batch, 0);
-  m->h_limit.assign(kv->batch, 0);
-  for (int b = 0; b < B; ++b) { m->h_lens[b] = la.lens[b]; m->h_limit[b] = la.limit[b]; }
+  if (pl.reset || m->h_lens.empty() || !same_kv(*kv, m->rec_kv)) {
+    m->rec_kv = *kv;
+    m->h_lens.assign(kv->batch, 0);
+    m->h_limit.assign(kv->batch, 0);
+  }
+  for (int b = 0; b < kv->batch; ++b) {
+    if (pl.la.lens[b] >= 0) m->h_lens[b] = pl.la.lens[b];
+    if (pl.la.limit[b] >= 0) m->h_limit[b] = pl.la.limit[b];
+  }
   return NGPT_OK;
 }
 
@@ -618,38 +736,11 @@ int ngpt_prefill(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
                  int32_t Tmax) {
   if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
   if (!ids) return fail(m, NGPT_E_ARG, "ids is NULL");
-  RowMap map{};
-  LensArgs la{};
-  int maxlen = 0;
-  int rc = plan_prefill(m, kv, lens, limit, B, Tmax, map, la, maxlen);
+  RowPlan pl;
+  int rc = plan_prompts(m, kv, nullptr, lens, limit, B, Tmax, true, pl);
+  if (rc == NGPT_OK) rc = stage_host_ids(m, pl, ids, Tmax);
   if (rc != NGPT_OK) return rc;
-  // every id on the host, before anything is enqueued
-  for (int b = 0; b < B; ++b)
-    for (int p = 0; p < lens[b]; ++p) {
-      const int32_t id = ids[(size_t)b * Tmax + p];
-      if (id < 0 || id >= m->V)
-        return fail(m, NGPT_E_RANGE, "prompt id outside [0, vocab_size)");
-    }
-  // pinned staging, packed, then an asynchronous copy to the workspace
-  const size_t half = (size_t)m->cfg.max_prefill_tokens;
-  if (!m->pinned) {
-    HIP_TRY(m, hipHostMalloc(reinterpret_cast<void**>(&m->pinned), 2 * half * sizeof(int32_t),
-                             hipHostMallocDefault));
-    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[0], hipEventDisableTiming));
-    HIP_TRY(m, hipEventCreateWithFlags(&m->pinned_ev[1], hipEventDisableTiming));
-  }
-  const int hf = m->pinned_half;
-  if (m->pinned_used[hf]) HIP_TRY(m, hipEventSynchronize(m->pinned_ev[hf]));
-  int32_t* stage = m->pinned + hf * half;
-  for (int b = 0; b < B; ++b)
-    memcpy(stage + map.off[b], ids + (size_t)b * Tmax, sizeof(int32_t) * lens[b]);
-  const int M = map.off[B];
-  HIP_TRY(m, hipMemcpyAsync(m->d_ids, stage, sizeof(int32_t) * M, hipMemcpyHostToDevice,
-                            m->stream));
-  HIP_TRY(m, hipEventRecord(m->pinned_ev[hf], m->stream));
-  m->pinned_used[hf] = true;
-  m->pinned_half = hf ^ 1;
-  return enqueue_prefill(m, kv, m->d_ids, 0, map, la, maxlen);
+  return enqueue_rows(m, kv, m->d_ids, 0, pl);
 }
 
 int ngpt_prefill_device(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
@@ -658,12 +749,95 @@ int ngpt_prefill_device(ngpt_model* m, ngpt_kv* kv, const int32_t* ids,
   if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
   if (!ids) return fail(m, NGPT_E_ARG, "ids is NULL");
   if (Tmax < 1) return fail(m, NGPT_E_ARG, "Tmax must be >= 1");
-  RowMap map{};
-  LensArgs la{};
-  int maxlen = 0;
-  int rc = plan_prefill(m, kv, lens, limit, B, Tmax, map, la, maxlen);
+  RowPlan pl;
+  int rc = plan_prompts(m, kv, nullptr, lens, limit, B, Tmax, true, pl);
   if (rc != NGPT_OK) return rc;
-  return enqueue_prefill(m, kv, ids, Tmax, map, la, maxlen);
+  return enqueue_rows(m, kv, ids, Tmax, pl);
+}
+
+int ngpt_prefill_slots(ngpt_model* m, ngpt_kv* kv, const int32_t* slots,
+                       const int32_t* ids, const int32_t* lens, const int32_t* limit,
+                       int32_t n, int32_t Tmax) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  if (!ids || !slots) return fail(m, NGPT_E_ARG, "ids or slots is NULL");
+  // a cache other than the recorded one starts with every row inactive
+  const bool fresh = m->h_lens.empty() || !kv || !same_kv(*kv, m->rec_kv);
+  RowPlan pl;
+  int rc = plan_prompts(m, kv, slots, lens, limit, n, Tmax, fresh, pl);
+  if (rc == NGPT_OK) rc = stage_host_ids(m, pl, ids, Tmax);
+  if (rc != NGPT_OK) return rc;
+  return enqueue_rows(m, kv, m->d_ids, 0, pl);
+}
+
+int ngpt_extend(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, const int32_t* ids,
+                const int32_t* counts, int32_t n, int32_t Tmax) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  if (!ids) return fail(m, NGPT_E_ARG, "ids is NULL");
+  RowPlan pl;
+  int rc = plan_extend(m, kv, slots, counts, n, Tmax, pl);
+  if (rc == NGPT_OK) rc = stage_host_ids(m, pl, ids, Tmax);
+  if (rc != NGPT_OK) return rc;
+  return enqueue_rows(m, kv, m->d_ids, 0, pl);
+}
+
+int ngpt_retire(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, int32_t n) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  int rc = check_kv(m, kv);
+  if (rc != NGPT_OK) return rc;
+  if (m->h_lens.empty() || !same_kv(*kv, m->rec_kv))
+    return fail(m, NGPT_E_ARG, "kv is not the cache of the last prefill on this model");
+  if (!slots || n < 1 || n > kv->batch) return fail(m, NGPT_E_ARG, "slots / n");
+  LensArgs la{};
+  la.n = kv->batch;
+  for (int b = 0; b < kv->batch; ++b) la.lens[b] = la.limit[b] = -1;
+  for (int i = 0; i < n; ++i) {
+    const int sl = slots[i];
+    if (sl < 0 || sl >= kv->batch) return fail(m, NGPT_E_RANGE, "slot outside [0, kv->batch)");
+    la.limit[sl] = m->h_lens[sl];   // no further tokens; the cache is kept
+  }
+  set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, m->stream>>>(la, kv->lens, kv->limit);
+  HIP_TRY(m, hipGetLastError());
+  for (int b = 0; b < kv->batch; ++b)
+    if (la.limit[b] >= 0) m->h_limit[b] = la.limit[b];
+  return NGPT_OK;
+}
+
+int ngpt_slide(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, int32_t n,
+               const int32_t* next_ids) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  int rc = check_kv(m, kv);
+  if (rc != NGPT_OK) return rc;
+  if (m->h_lens.empty() || !same_kv(*kv, m->rec_kv))
+    return fail(m, NGPT_E_ARG, "kv is not the cache of the last prefill on this model");
+  if (!slots || !next_ids || n < 1 || n > kv->batch) return fail(m, NGPT_E_ARG, "slots / ids / n");
+  if ((long)n * m->Tb > m->cfg.max_prefill_tokens)
+    return fail(m, NGPT_E_SIZE, "n * block_size > max_prefill_tokens");
+  RowPlan pl;
+  pl.map.B = n;
+  pl.la.n = kv->batch;
+  for (int b = 0; b < kv->batch; ++b) pl.la.lens[b] = pl.la.limit[b] = -1;
+  SlotList sl{};
+  sl.n = n;
+  std::vector<char> seen(kv->batch, 0);
+  for (int i = 0; i < n; ++i) {
+    const int b = slots[i];
+    if (b < 0 || b >= kv->batch) return fail(m, NGPT_E_RANGE, "slot outside [0, kv->batch)");
+    if (seen[b]) return fail(m, NGPT_E_ARG, "a slot is listed twice");
+    seen[b] = 1;
+    if (m->h_lens[b] != m->Tb)
+      return fail(m, NGPT_E_ARG, "slide needs a row whose cache holds block_size positions");
+    sl.slot[i] = b;
+    pl.map.off[i] = i * m->Tb;
+    pl.map.slot[i] = b;
+    pl.map.past[i] = 0;
+    pl.la.lens[b] = m->Tb;
+  }
+  pl.map.off[n] = n * m->Tb;
+  pl.maxlen = m->Tb;
+  const dim3 g((m->Tb + 255) / 256, n);
+  window_ids_kernel<<<g, 256, 0, m->stream>>>(sl, m->hist, m->Tb, next_ids, m->d_ids);
+  HIP_TRY(m, hipGetLastError());
+  return enqueue_rows(m, kv, m->d_ids, 0, pl);
 }
 
 }  // extern "C"
@@ -689,6 +863,7 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
   a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
   a.epoch = m->epoch; a.done = m->done; a.status = m->status;
+  a.hist = m->hist;
   a.wait_limit = m->h_wait_limit;
   return a;
 }
@@ -749,6 +924,8 @@ static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
   a.lens = kv->lens;
   a.limit = kv->limit;
   a.status = m->status;
+  a.hist = m->hist;
+  a.Tb = m->Tb;
   a.wte = m->wte;
   a.wpe = m->wpe;
   a.C = m->C;

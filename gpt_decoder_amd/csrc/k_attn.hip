@@ -40,6 +40,10 @@ constexpr int kPrefillKch = 4;   // key tiles per chunk when a prefill tile is s
 // from a transposed LDS copy in the same key order.
 // ---------------------------------------------------------------------------
 //
+// With a past (chunked prefill into a live cache) the new rows of a
+// sequence sit at positions past .. past + len - 1 and each sees every key
+// up to its own position (the offset causal mask); without one, past = 0.
+//
 // Key split (kch > 0, batch 1): a query tile that meets more than kch key
 // tiles is split into chunks of kch key tiles, one workgroup each; such a
 // chunk leaves its rows' unnormalised state (m, l, o) in part, and
@@ -60,21 +64,27 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int len = map.off[b + 1] - map.off[b];
+  const int past = map.past[b];
   const int ntiles = (len + 63) / 64;
   const int qt = ntiles - 1 - (kch > 0 ? (int)blockIdx.x / nsplit : (int)blockIdx.x);
   if (qt < 0) return;
-  // key tiles [kt0, kt1) of this workgroup
-  const int nch = kch > 0 ? (qt + kch) / kch : 1;
+  const int q0 = qt * 64;
+  // key tiles this query tile meets: 0 .. (its last row's position) / 64
+  const int nkt_all = (past + min(q0 + 63, len - 1)) / KT + 1;
+  // key tiles [kt0, kt0 + nkt) of this workgroup
+  const int nch = kch > 0 ? (nkt_all + kch - 1) / kch : 1;
   const int chunk = kch > 0 ? (int)blockIdx.x % nsplit : 0;
   if (chunk >= nch) return;
   const int kt0 = kch > 0 ? chunk * kch : 0;
-  const int q0 = qt * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;                       // lane group 0..3
-  const int qrow = q0 + wave * 16 + (lane & 15);  // this lane's query
+  const int qrow = q0 + wave * 16 + (lane & 15);  // this lane's query (new row)
+  const int qpos = past + qrow;                   // ... and its position
+  const int kend = past + len;                    // keys in the cache
   const size_t row0 = (size_t)map.off[b];
-  const bf16_t* kbase = kc + ((size_t)b * H + h) * Tb * HS;
-  const bf16_t* vbase = vc + ((size_t)b * H + h) * Tb * HS;
+  const int slot = map.slot[b];
+  const bf16_t* kbase = kc + ((size_t)slot * H + h) * Tb * HS;
+  const bf16_t* vbase = vc + ((size_t)slot * H + h) * Tb * HS;
 
   // Q^T operand: column = this lane's query, K-values = dims 8g.. (+32 kk)
   bf16x8_t qf[NKK];
@@ -92,8 +102,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int last_key = min(q0 + 63, len - 1);
-  const int nkt = (nch > 1 ? min(kt0 + kch, qt + 1) : last_key / KT + 1) - kt0;
+  const int nkt = (nch > 1 ? min(kt0 + kch, nkt_all) : nkt_all) - kt0;
   // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
   // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
   // S tiles are in flight in registers.  The loads are range-checked buffer
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const int key = k0 + 2 * kp + e2;
-        const uint32_t off = (c < ITEMS && key < len) ? ((uint32_t)key * HS + d0) * 2u : kOut;
+        const uint32_t off = (c < ITEMS && key < kend) ? ((uint32_t)key * HS + d0) * 2u : kOut;
         rk[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, off, 0, 0));
         rv[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, off, 0, 0));
       }
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + t * 16 + g * 4 + i;
-        const float v = (key <= qrow) ? s[t][i] * sl2 : -INFINITY;
+        const float v = (key <= qpos) ? s[t][i] * sl2 : -INFINITY;
         s[t][i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -248,16 +257,19 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 
 // Merge of a split query tile's chunks (batch 1): one wavefront per (row,
 // head), four rows per workgroup; lane d merges dimension d over the chunks
-// in chunk order.
+// in chunk order.  Rows whose tile had a single chunk were written directly.
 constexpr int kMergeRows = 4;
 template <int HS>
 __global__ __launch_bounds__(64 * kMergeRows) void attn_prefill_merge(
-    const float* __restrict__ part, int len, int Tb, int kch, int nsplit,
-    bf16_t* __restrict__ y, int ldy) {
-  const int row = kch * 64 + (int)blockIdx.x * kMergeRows + (int)(threadIdx.x >> 6);
+    const float* __restrict__ part, int len, int past, int Tb, int kch, int nsplit,
+    bf16_t* __restrict__ y, int ldy, int r0) {
+  const int row = r0 + (int)blockIdx.x * kMergeRows + (int)(threadIdx.x >> 6);
   const int h = blockIdx.y, d = threadIdx.x & 63;
   if (row >= len || d >= HS) return;
-  const int nch = (row / 64 + kch) / kch;
+  const int q0 = (row / 64) * 64;
+  const int nkt_all = (past + min(q0 + 63, len - 1)) / 64 + 1;
+  const int nch = (nkt_all + kch - 1) / kch;
+  if (nch <= 1) return;
   const float* pp = part + ((size_t)h * Tb + row) * nsplit * (HS + 4);
   float m = pp[0], l = pp[1], o = pp[4 + d];
   for (int c = 1; c < nch; ++c) {
@@ -277,11 +289,12 @@ __global__ __launch_bounds__(64) void attn_prefill_simt(
     T* __restrict__ y, int ldy) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int len = map.off[b + 1] - map.off[b];
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  if (t >= len) return;
-  const size_t row = (size_t)map.off[b] + t;
-  const T* kbase = kc + ((size_t)b * H + h) * Tb * HS;
-  const T* vbase = vc + ((size_t)b * H + h) * Tb * HS;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= len) return;
+  const int t = map.past[b] + i;        // position: sees keys 0 .. t
+  const size_t row = (size_t)map.off[b] + i;
+  const T* kbase = kc + ((size_t)map.slot[b] * H + h) * Tb * HS;
+  const T* vbase = vc + ((size_t)map.slot[b] * H + h) * Tb * HS;
   float qv[HS], acc[HS];
 #pragma unroll
   for (int d = 0; d < HS; ++d) {
@@ -466,9 +479,11 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
   if (dtype == NGPT_BF16) {
     const bf16_t* qq = (const bf16_t*)q;
     // one sequence with few workgroups: split the long query tiles' keys
-    const bool split = part && map.B == 1 && ntiles > kPrefillKch && ntiles * H < 256;
+    const int past = map.past[0];
+    const int nkt_max = (past + maxlen - 1) / 64 + 1;
+    const bool split = part && map.B == 1 && nkt_max > kPrefillKch && ntiles * H < 256;
     const int kch = split ? kPrefillKch : 0;
-    const int nsplit = split ? (ntiles + kPrefillKch - 1) / kPrefillKch : 1;
+    const int nsplit = split ? (nkt_max + kPrefillKch - 1) / kPrefillKch : 1;
     const dim3 grid(ntiles * nsplit, H, map.B);
     if (hs == 64)
       attn_prefill_mfma<64><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
@@ -477,13 +492,20 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
       attn_prefill_mfma<32><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
           (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
     if (split) {
-      const dim3 mgrid((maxlen - kch * 64 + kMergeRows - 1) / kMergeRows, H);
+      // rows of single-chunk tiles need no merge: start at the first tile
+      // with more than one chunk
+      int first = 0;
+      while (first < ntiles && (past + min(first * 64 + 63, maxlen - 1)) / 64 + 1 <= kch) ++first;
+      const int r0 = first * 64;
+      const dim3 mgrid((maxlen - r0 + kMergeRows - 1) / kMergeRows, H);
+      const float* pp = part;
+      bf16_t* yy = (bf16_t*)y;
       if (hs == 64)
-        attn_prefill_merge<64><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, Tb, kch, nsplit,
-                                                                (bf16_t*)y, ldy);
+        attn_prefill_merge<64><<<mgrid, 64 * kMergeRows, 0, s>>>(pp, maxlen, past, Tb, kch, nsplit,
+                                                                yy, ldy, r0);
       else
-        attn_prefill_merge<32><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, Tb, kch, nsplit,
-                                                                (bf16_t*)y, ldy);
+        attn_prefill_merge<32><<<mgrid, 64 * kMergeRows, 0, s>>>(pp, maxlen, past, Tb, kch, nsplit,
+                                                                yy, ldy, r0);
     }
   } else {
     const dim3 grid(ntiles, H, map.B);

@@ -18,6 +18,7 @@ __global__ __launch_bounds__(256) void embed_prefill_kernel(
     const T* __restrict__ wte, const T* __restrict__ wpe, int C, int V,
     float* __restrict__ x, int32_t* __restrict__ row_b,
     int32_t* __restrict__ row_pos, int32_t* __restrict__ last_rows,
+    int32_t* __restrict__ last_slot, int32_t* __restrict__ hist, int Tb,
     int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   // sequence owning packed row r: the last b with off[b] <= r
@@ -27,16 +28,21 @@ __global__ __launch_bounds__(256) void embed_prefill_kernel(
     if (map.off[mid] <= r) lo = mid; else hi = mid - 1;
   }
   const int b = lo;
-  const int p = r - map.off[b];
-  int id = ids[Tmax > 0 ? (size_t)b * Tmax + p : (size_t)r];
+  const int i = r - map.off[b];          // index among the sequence's new rows
+  const int p = map.past[b] + i;         // its position
+  int id = ids[Tmax > 0 ? (size_t)b * Tmax + i : (size_t)r];
   if (id < 0 || id >= V) {
     if (threadIdx.x == 0) atomicOr(status, 1);
     id = 0;
   }
   if (threadIdx.x == 0) {
-    row_b[r] = b;
+    row_b[r] = map.slot[b];
     row_pos[r] = p;
-    if (r == map.off[b + 1] - 1) last_rows[b] = r;
+    hist[(size_t)map.slot[b] * Tb + p] = id;
+    if (r == map.off[b + 1] - 1) {
+      last_rows[b] = r;
+      last_slot[b] = map.slot[b];
+    }
   }
   const T* te = wte + (size_t)id * C;
   const T* pe = wpe + (size_t)p * C;
@@ -147,16 +153,17 @@ void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
                           const RowMap& map, int M, const void* wte,
                           const void* wpe, int C, int V, float* x,
                           int32_t* row_b, int32_t* row_pos, int32_t* last_rows,
+                          int32_t* last_slot, int32_t* hist, int Tb,
                           int32_t* status, hipStream_t s) {
   if (M <= 0) return;
   if (dtype == NGPT_BF16)
     embed_prefill_kernel<bf16_t><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const bf16_t*)wte, (const bf16_t*)wpe, C, V, x,
-        row_b, row_pos, last_rows, status);
+        row_b, row_pos, last_rows, last_slot, hist, Tb, status);
   else
     embed_prefill_kernel<float><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const float*)wte, (const float*)wpe, C, V, x, row_b,
-        row_pos, last_rows, status);
+        row_pos, last_rows, last_slot, hist, Tb, status);
 }
 
 void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,

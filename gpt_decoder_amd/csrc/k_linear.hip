@@ -29,7 +29,8 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
                                           float acc) {
   if constexpr (EPI == EPI_LOGITS) {
     if (e.row_pos && e.row_pos[r] < 0) return;
-    static_cast<float*>(e.out)[(size_t)r * e.ldo + n] = acc;
+    const int orow = e.row_b ? e.row_b[r] : r;   // the sequence's logits row
+    static_cast<float*>(e.out)[(size_t)orow * e.ldo + n] = acc;
     return;
   } else {
     float v = acc;

@@ -593,6 +593,7 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
           a.next_ids[0] = tok;
           a.tok[0] = tok;
           a.pos[0] = p;
+          a.hist[p] = tok;
         }
       }
       __syncthreads();

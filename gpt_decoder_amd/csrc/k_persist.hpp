@@ -24,6 +24,7 @@ struct PersistArgs {
   const int32_t* limit;         // kv limit [1] (fused: lens >= limit => inactive)
   int32_t* tok;                 // fused: the chosen id ...
   int32_t* next_ids;            // ... and the caller's copy
+  int32_t* hist;                // fused: token history [1][Tb] (id at p)
   uint64_t* e_cand;             // greedy candidates, 2 words per workgroup
   const float* x0;              // [C] embedding written by the head node
   bf16_t* kc;                   // cache bases and per-layer stride (elements)

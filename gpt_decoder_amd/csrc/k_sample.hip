@@ -219,7 +219,8 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     const int32_t* __restrict__ feed_ids, int32_t* __restrict__ next_ids,
     int32_t* __restrict__ tok, int32_t* __restrict__ pos,
     int32_t* __restrict__ lens, const int32_t* __restrict__ limit,
-    int32_t* __restrict__ status, const void* __restrict__ wte,
+    int32_t* __restrict__ status, int32_t* __restrict__ hist, int Tb,
+    const void* __restrict__ wte,
     const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x) {
   __shared__ SampShared sh;
   const int b = blockIdx.x;
@@ -265,6 +266,7 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
       tok[b] = id;
       pos[b] = len;
       lens[b] = len + 1;
+      hist[(size_t)b * Tb + len] = id;
     }
   }
   if (mode != SAMPLE_ONLY) {
@@ -277,10 +279,11 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
 }
 
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p) {
-  void* vals[18] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
+  void* vals[20] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
                     &a.feed_ids, &a.next_ids, &a.tok, &a.pos, &a.lens,
-                    &a.limit, &a.status, &a.wte, &a.wpe, &a.C, &a.dtype, &a.x};
-  for (int i = 0; i < 18; ++i) a.ptrs[i] = vals[i];
+                    &a.limit, &a.status, &a.hist, &a.Tb, &a.wte, &a.wpe, &a.C,
+                    &a.dtype, &a.x};
+  for (int i = 0; i < 20; ++i) a.ptrs[i] = vals[i];
   p->func = reinterpret_cast<void*>(sampler_kernel);
   p->gridDim = dim3(B);
   p->blockDim = dim3(a.mode == FEED_STEP ? 256 : kSampThreads);
@@ -294,8 +297,9 @@ void launch_sampler(const SamplerArgs& a, int B, hipStream_t s) {
   const int threads = (a.mode == FEED_STEP) ? 256 : kSampThreads;
   sampler_kernel<<<B, threads, 0, s>>>(a.mode, a.logits, a.ld, a.V, a.uniforms,
                                        a.params, a.feed_ids, a.next_ids, a.tok,
-                                       a.pos, a.lens, a.limit, a.status, a.wte,
-                                       a.wpe, a.C, a.dtype, a.x);
+                                       a.pos, a.lens, a.limit, a.status,
+                                       a.hist, a.Tb, a.wte, a.wpe, a.C,
+                                       a.dtype, a.x);
 }
 
 }  // namespace ngpt

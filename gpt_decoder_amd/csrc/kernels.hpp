@@ -12,10 +12,14 @@ typedef uint16_t bf16_t;
 
 namespace ngpt {
 
-// Packed prefill rows: sequence b owns rows [off[b], off[b+1]).
+// Packed prefill rows: sequence b owns rows [off[b], off[b+1]); they go to
+// cache row (slot) slot[b] at positions past[b] .. past[b] + (its row count)
+// - 1, after the past[b] positions already cached there.
 struct RowMap {
   int32_t B;
   int32_t off[NGPT_MAX_BATCH + 1];
+  int32_t slot[NGPT_MAX_BATCH];
+  int32_t past[NGPT_MAX_BATCH];
 };
 
 // Linear-layer epilogues (what happens to acc = A W^T for row r, column n).
@@ -23,7 +27,7 @@ enum Epi {
   EPI_GELU = 1,    // out[r][n] = GELU(acc + bias)                (dtype)
   EPI_RESID = 2,   // out[r][n] += acc + bias                      (fp32 residual)
   EPI_QKV = 3,     // split into q (out, dtype) and the K/V cache rows
-  EPI_LOGITS = 4,  // out[r][n] = acc                             (fp32)
+  EPI_LOGITS = 4,  // out[row_b ? row_b[r] : r][n] = acc          (fp32)
 };
 
 struct EpiArgs {
@@ -53,11 +57,15 @@ enum SampleMode {
   FEED_STEP = 2,    // teacher forcing: ids given, set tok/pos, advance lens
 };
 
-// ids: [B][Tmax] right-padded (Tmax > 0) or packed by row (Tmax == 0)
+// ids: [B][Tmax] right-padded (Tmax > 0) or packed by row (Tmax == 0).
+// Writes x, the row -> (slot, position) maps, each sequence's last row and
+// its slot (last_rows[b], last_slot[b]), and the ids into the token history
+// hist [max_batch][Tb] (slot, position).
 void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
                           const RowMap& map, int M, const void* wte,
                           const void* wpe, int C, int V, float* x,
                           int32_t* row_b, int32_t* row_pos, int32_t* last_rows,
+                          int32_t* last_slot, int32_t* hist, int Tb,
                           int32_t* status, hipStream_t s);
 
 void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,
@@ -130,13 +138,15 @@ struct SamplerArgs {
   int32_t* lens = nullptr;
   const int32_t* limit = nullptr;
   int32_t* status = nullptr;
+  int32_t* hist = nullptr;   // token history [B][Tb]: the step's id at pos
+  int Tb = 0;
   // decode steps also write the embedding x = wte[id] + wpe[pos] (fp32 [B][C])
   const void* wte = nullptr;
   const void* wpe = nullptr;
   int C = 0;
   int dtype = 0;
   float* x = nullptr;
-  void* ptrs[18] = {};
+  void* ptrs[20] = {};
 };
 // Fill a kernel-node description for B rows; `a` must outlive its use.
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);

@@ -232,6 +232,61 @@ int ngpt_prefill_device(ngpt_model *m, ngpt_kv *kv, const int32_t *ids,
                         int32_t Tmax);
 
 /*
+ * Admit prompts into chosen rows of a live batch (continuous batching: new
+ * sequences take the rows of finished ones while the others keep their
+ * state; serving page, section "HF 在哪些情况下实际上会更好" on batched
+ * serving, and the KV-cache section for the per-row cache).  Like
+ * ngpt_prefill for n prompts (host ids [n][Tmax], lens, limit), but prompt b
+ * goes to kv row slots[b] (distinct, < kv->batch) from an empty cache, and
+ * every other row keeps its cache, lens, limit and logits.  When kv is not
+ * the cache of the last prefill on this model, every other row is made
+ * inactive instead.  Errors: as ngpt_prefill; NGPT_E_RANGE for a slot out
+ * of range, NGPT_E_ARG for a repeated slot.
+ */
+int ngpt_prefill_slots(ngpt_model *m, ngpt_kv *kv, const int32_t *slots,
+                       const int32_t *ids, const int32_t *lens,
+                       const int32_t *limit, int32_t n, int32_t Tmax);
+
+/*
+ * Chunked prefill into a live cache: append counts[b] tokens (host ids
+ * [n][Tmax], row b) to live row slots[b] of the cache of the last prefill,
+ * at positions lens .. lens + counts[b] - 1.  Each new token attends to every
+ * cached position and to the new tokens up to itself: the causal mask offset
+ * by the past length, which the serving page's KV-cache sketch leaves out
+ * (it masks only when there is no past).  Leaves the logits of each row's
+ * last new token.  Requires lens + counts[b] <= limit of the row.
+ * Errors: NGPT_E_ARG, NGPT_E_RANGE (ids, slots, counts), NGPT_E_CONTEXT (the
+ * row's limit), NGPT_E_SIZE (sum(counts) > max_prefill_tokens), NGPT_E_HIP.
+ */
+int ngpt_extend(ngpt_model *m, ngpt_kv *kv, const int32_t *slots,
+                const int32_t *ids, const int32_t *counts, int32_t n,
+                int32_t Tmax);
+
+/*
+ * Retire rows of the cache of the last prefill: each listed row stops taking
+ * tokens (its limit becomes its length; cache and logits are kept), so its
+ * row can be admitted again with ngpt_prefill_slots.  Errors: NGPT_E_ARG,
+ * NGPT_E_RANGE, NGPT_E_HIP.
+ */
+int ngpt_retire(ngpt_model *m, ngpt_kv *kv, const int32_t *slots, int32_t n);
+
+/*
+ * Generation past block_size (generate() crops its input to the last
+ * block_size tokens, serving page section 2): for each listed row whose cache
+ * holds block_size positions, the window of its cached tokens 1 .. Tb-1
+ * followed by next_ids[row] (device int32 [kv->batch], e.g. drawn by
+ * ngpt_sample from the row's logits) is run again from position 0 (the
+ * positions are absolute, so the cache cannot be shifted), which refreshes
+ * the row's cache and leaves the logits of the window's last token.  The
+ * row's tokens come from the library's token history, written by every
+ * prefill and decode call.  Requires n * block_size <= max_prefill_tokens.
+ * Errors: NGPT_E_ARG (a row that is not full, kv not the recorded cache),
+ * NGPT_E_RANGE, NGPT_E_SIZE, NGPT_E_HIP.
+ */
+int ngpt_slide(ngpt_model *m, ngpt_kv *kv, const int32_t *slots, int32_t n,
+               const int32_t *next_ids);
+
+/*
  * One decode step for all kv->batch sequences (the loop body of generate()
  * in the serving page, section 2, with the KV cache of its "一个值得做的改进"
  * section: only the newest token is run, against the cached K/V): for every

@@ -283,6 +283,28 @@ class OracleGPT:
             out[b] = self._head(x)[0]
         return out
 
+    def admit(self, slot: int, ids: Sequence[int]) -> np.ndarray:
+        """Start sequence ``slot`` over from an empty cache with prompt
+        ``ids`` (the other sequences keep their caches); returns the logits
+        [V] at the prompt's last position.  Continuous batching: a finished
+        sequence's place is reused (serving page, section "HF 在哪些情况下
+        实际上会更好")."""
+        while len(self.caches) <= slot:
+            self.caches.append(_SeqCache(self.L, self.C, self.dt))
+        self.caches[slot] = _SeqCache(self.L, self.C, self.dt)
+        x = self._forward_rows(np.asarray(ids), self.caches[slot])
+        return self._head(x[-1:])[0]
+
+    def extend(self, slot: int, ids: Sequence[int]) -> np.ndarray:
+        """Append the tokens ``ids`` to sequence ``slot``'s cache in one
+        forward (a chunk of new rows with a past); returns the logits [V] at
+        the last new position.  The new rows see the whole past and each
+        other causally: ``causal_attention`` with past_len = the cache
+        length (serving page, KV-cache section, extended to several new
+        tokens)."""
+        x = self._forward_rows(np.asarray(ids), self.caches[slot])
+        return self._head(x[-1:])[0]
+
     def lengths(self) -> List[int]:
         return [c.length for c in self.caches]
 
@@ -303,6 +325,12 @@ class OracleGPT:
         col: dict = {}
         self._forward_rows(np.asarray(ids), cache, collect=col)
         return col.get("x", [])
+
+    def window_logits(self, tokens: Sequence[int]) -> np.ndarray:
+        """generate()'s crop (serving page, section 2): the logits [V] of
+        the last position of the last block_size tokens, run from position
+        0 with no cache."""
+        return self.full_logits(list(tokens)[-self.Tb:])[0]
 
     def generate_greedy(self, prompt: Sequence[int], steps: int):
         """KV-cached greedy generation for one sequence: returns the new

@@ -268,24 +268,26 @@ def test_gpt2_xl_batch32_full():
     m.close()
     got = np.array(got)            # [513 positions 511..1023][rows][V]
     toks = np.array(toks)          # [512][batch]
-    o = make_oracle(w, W)
-    errs, need_n, agree_n = [], 0, 0
+    o, ox = make_oracle(w, W), make_exact_oracle(w, W)
+    errs, errx, need_n, agree_n = [], [], 0, 0
     for b in rows:
         seq = [int(t) for t in ids[b, :512]] + [int(t) for t in toks[:, b]]
-        with Timer(f"  oracle bf16-mode row {b}"):
+        with Timer(f"  oracle row {b}, both modes"):
             ref = o.full_logits(seq, positions=list(range(511, 1024)))
+            rex = ox.full_logits(seq, positions=list(range(511, 1024)))
         errs.append(max_abs(got[:, b], ref))
+        errx.append(max_abs(got[:, b], rex))
         need = greedy_must_agree(ref[:w.steps], TOL_BF16)
         agree = np.argmax(ref[:w.steps], axis=1) == toks[:, b]
         need_n += int(need.sum())
         agree_n += int(agree.sum())
         assert agree[need].all(), f"row {b}"
-        if b == 0:
-            with Timer("  oracle exact row 0"):
-                rex = make_exact_oracle(w, W).full_logits(seq, positions=list(range(511, 1024)))
-            errx = max_abs(got[:, 0], rex)
-            log(f"  row 0 vs exact oracle: {errx:.2e}")
-    log(f"  logit errs vs bf16-mode {['%.2e' % e for e in errs]}; margin-qualified "
-        f"greedy steps {need_n}/{len(rows) * w.steps} all agree; raw agreement "
+    log(f"  logit errs vs exact {['%.2e' % e for e in errx]}; vs bf16-mode "
+        f"{['%.2e' % e for e in errs]}; margin-qualified greedy steps "
+        f"{need_n}/{len(rows) * w.steps} all agree; raw agreement "
         f"{agree_n}/{len(rows) * w.steps}")
-    assert max(errs) < TOL_BF16
+    # The bar is the model as defined (the exact oracle).  The bf16-mode
+    # oracle is one bf16 data path among many; at 48 blocks two such paths
+    # differ by ~2e-2 from their rounding decisions alone, so its distance is
+    # reported, not held to the bar.
+    assert max(errx) < TOL_BF16

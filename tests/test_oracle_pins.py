@@ -305,6 +305,47 @@ def test_kv_decode_equals_full_recompute():
     np.testing.assert_allclose(np.array(logits), full, rtol=0, atol=1e-12)
 
 
+def test_extend_in_chunks_equals_full_recompute():
+    """Prefill of a prefix, then chunks of several new tokens at a time (the
+    causal mask offset by the past length), give the full-prefix forward's
+    logits at each chunk's last position."""
+    cfg = small_cfg(L=3, Tb=64, bias=True)
+    w = synth.make_weights(cfg, gamma_std=0.1)
+    ids = rng.integers(0, cfg.vocab_size, 50)
+    o = OracleGPT(cfg, w)
+    o.admit(0, ids[:7])
+    cuts = [7, 8, 21, 40, 50]
+    full = OracleGPT(cfg, w).full_logits(ids, positions=[c - 1 for c in cuts[1:]])
+    for (a, b), want in zip(zip(cuts[:-1], cuts[1:]), full):
+        np.testing.assert_allclose(o.extend(0, ids[a:b]), want, rtol=0, atol=1e-12)
+    assert o.lengths() == [50]
+
+
+def test_admit_restarts_one_sequence_only():
+    cfg = small_cfg(L=2, Tb=32)
+    w = synth.make_weights(cfg)
+    ids = rng.integers(0, cfg.vocab_size, (2, 12)).astype(np.int32)
+    o = OracleGPT(cfg, w)
+    o.prefill(ids, [12, 12])
+    o.decode([3, 4])
+    fresh = o.admit(1, [5, 6, 7])
+    np.testing.assert_allclose(fresh, OracleGPT(cfg, w).full_logits([5, 6, 7])[0],
+                               rtol=0, atol=1e-12)
+    assert o.lengths() == [13, 3]
+    got = o.decode([9, 9])
+    want0 = OracleGPT(cfg, w).full_logits(list(ids[0]) + [3, 9])[0]
+    np.testing.assert_allclose(got[0], want0, rtol=0, atol=1e-12)
+
+
+def test_window_logits_is_the_crop_of_the_last_block():
+    cfg = small_cfg(L=2, Tb=16)
+    w = synth.make_weights(cfg)
+    toks = list(rng.integers(0, cfg.vocab_size, 40))
+    o = OracleGPT(cfg, w)
+    np.testing.assert_array_equal(o.window_logits(toks), o.full_logits(toks[-16:])[0])
+    np.testing.assert_array_equal(o.window_logits(toks[:10]), o.full_logits(toks[:10])[0])
+
+
 def test_batch_rows_are_independent_and_ragged():
     cfg = small_cfg(bias=True)
     w = synth.make_weights(cfg)
