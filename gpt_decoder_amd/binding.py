@@ -96,6 +96,8 @@ def lib():
                                      ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      i32, i32]
     L.ngpt_extend.argtypes = [vp, ctypes.POINTER(KV), vp, vp, vp, i32, i32]
+    L.ngpt_eval_loss.argtypes = [vp, ctypes.POINTER(KV), vp, ctypes.POINTER(i32),
+                                 i32, i32, vp, vp, vp]
     L.ngpt_retire.argtypes = [vp, ctypes.POINTER(KV), vp, i32]
     L.ngpt_slide.argtypes = [vp, ctypes.POINTER(KV), vp, i32, vp]
     L.ngpt_decode_step.argtypes = [vp, ctypes.POINTER(KV), vp, vp]
@@ -112,6 +114,7 @@ def lib():
     for name in ("ngpt_check_config", "ngpt_create", "ngpt_destroy",
                  "ngpt_set_sampling", "ngpt_prefill", "ngpt_prefill_device",
                  "ngpt_prefill_slots", "ngpt_extend", "ngpt_retire", "ngpt_slide",
+                 "ngpt_eval_loss",
                  "ngpt_decode_step",
                  "ngpt_decode_feed", "ngpt_sample", "ngpt_logits",
                  "ngpt_copy_logits", "ngpt_device_status", "ngpt_set_wait_limit"):
@@ -291,6 +294,24 @@ class Model:
             self.h, ctypes.byref(kv.struct), sl.ctypes.data_as(ctypes.c_void_p),
             a.ctypes.data_as(ctypes.c_void_p), c.ctypes.data_as(ctypes.c_void_p),
             n, Tmax))
+
+    def eval_loss(self, kv: KVCache, ids, lens, logits=None):
+        """Forward with labels over every position (host ids [B, Tmax]).
+        Returns (logits [sum(lens), V], losses [sum(lens)], mean [1]), all
+        device fp32; ``logits`` may be given to reuse a buffer."""
+        a = self._host_i32(ids)
+        B, Tmax = a.shape
+        M = int(sum(int(x) for x in lens))
+        t = self.torch
+        if logits is None:
+            logits = t.empty((M, self.vocab), dtype=t.float32, device=self.device)
+        losses = t.empty(M, dtype=t.float32, device=self.device)
+        mean = t.empty(1, dtype=t.float32, device=self.device)
+        lens_a = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+        self._check(lib().ngpt_eval_loss(
+            self.h, ctypes.byref(kv.struct), a.ctypes.data_as(ctypes.c_void_p),
+            lens_a, B, Tmax, _ptr(logits), _ptr(losses), _ptr(mean)))
+        return logits, losses, mean
 
     def retire(self, kv: KVCache, slots):
         sl = self._host_i32(slots)

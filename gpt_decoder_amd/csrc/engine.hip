@@ -672,13 +672,13 @@ static int stage_host_ids(ngpt_model* m, const RowPlan& pl, const int32_t* ids, 
   return NGPT_OK;
 }
 
-// The prefill launch sequence over the plan's rows.  ids: device; Tmax > 0
+// The blocks of the prefill launch sequence over the plan's rows: x holds
+// the final residual stream of every row afterwards.  ids: device; Tmax > 0
 // gives the [B][Tmax] right-padded layout, Tmax == 0 the packed layout.
-// Leaves the logits of each sequence's last new row in its slot's row.
-static int enqueue_rows(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
-                        const RowPlan& pl) {
+static void enqueue_blocks(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
+                           const RowPlan& pl) {
   const RowMap& map = pl.map;
-  const int M = map.off[map.B], C = m->C, dt = m->cfg.dtype, B = map.B;
+  const int M = map.off[map.B], C = m->C, dt = m->cfg.dtype;
   hipStream_t s = m->stream;
   m->cand_ok = false;   // the logits are about to come from this prefill
   set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(pl.la, kv->lens, kv->limit);
@@ -708,15 +708,10 @@ static int enqueue_rows(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax
     em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
     launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, M, C, 4 * C, em, s);
   }
-  // ln_f and the tied lm_head on each sequence's last row only, into the
-  // logits row of its slot
-  launch_layernorm(dt, m->x, C, m->last_rows, B, m->lnf_w, m->lnf_b, m->z, C, C, s);
-  EpiArgs el;
-  el.out = m->logits; el.ldo = m->V; el.row_b = m->last_slot;
-  launch_linear(dt, EPI_LOGITS, m->z, C, nullptr, m->wte, B, m->V, C, el, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+}
 
+// Record the plan's lens / limit on the host.
+static void record_plan(ngpt_model* m, const ngpt_kv* kv, const RowPlan& pl) {
   if (pl.reset || m->h_lens.empty() || !same_kv(*kv, m->rec_kv)) {
     m->rec_kv = *kv;
     m->h_lens.assign(kv->batch, 0);
@@ -726,6 +721,22 @@ static int enqueue_rows(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax
     if (pl.la.lens[b] >= 0) m->h_lens[b] = pl.la.lens[b];
     if (pl.la.limit[b] >= 0) m->h_limit[b] = pl.la.limit[b];
   }
+}
+
+// The prefill launch sequence: the blocks, then ln_f and the tied lm_head on
+// each sequence's last new row, into the logits row of its slot.
+static int enqueue_rows(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int Tmax,
+                        const RowPlan& pl) {
+  const int C = m->C, dt = m->cfg.dtype, B = pl.map.B;
+  hipStream_t s = m->stream;
+  enqueue_blocks(m, kv, ids, Tmax, pl);
+  launch_layernorm(dt, m->x, C, m->last_rows, B, m->lnf_w, m->lnf_b, m->z, C, C, s);
+  EpiArgs el;
+  el.out = m->logits; el.ldo = m->V; el.row_b = m->last_slot;
+  launch_linear(dt, EPI_LOGITS, m->z, C, nullptr, m->wte, B, m->V, C, el, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+  record_plan(m, kv, pl);
   return NGPT_OK;
 }
 
@@ -778,6 +789,35 @@ int ngpt_extend(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, const int32_t*
   if (rc == NGPT_OK) rc = stage_host_ids(m, pl, ids, Tmax);
   if (rc != NGPT_OK) return rc;
   return enqueue_rows(m, kv, m->d_ids, 0, pl);
+}
+
+int ngpt_eval_loss(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, const int32_t* lens,
+                   int32_t B, int32_t Tmax, float* logits, float* losses, float* mean_loss) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  if (!ids || !logits || !losses || !mean_loss)
+    return fail(m, NGPT_E_ARG, "ids, logits, losses or mean_loss is NULL");
+  RowPlan pl;
+  int rc = plan_prompts(m, kv, nullptr, lens, nullptr, B, Tmax, true, pl);
+  if (rc == NGPT_OK) rc = stage_host_ids(m, pl, ids, Tmax);
+  if (rc != NGPT_OK) return rc;
+  const int M = pl.map.off[B], C = m->C, dt = m->cfg.dtype;
+  hipStream_t s = m->stream;
+  m->cand_ok = false;
+  enqueue_blocks(m, kv, m->d_ids, 0, pl);
+  // ln_f and the tied lm_head on every row (the h rows hold M x C)
+  launch_layernorm(dt, m->x, C, nullptr, M, m->lnf_w, m->lnf_b, m->h, C, C, s);
+  EpiArgs el;
+  el.out = logits; el.ldo = m->V;
+  launch_linear(dt, EPI_LOGITS, m->h, C, nullptr, m->wte, M, m->V, C, el, s);
+  launch_cross_entropy(logits, m->V, m->V, M, M - B, m->d_ids, m->row_b, m->last_rows,
+                       losses, mean_loss, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(m, NGPT_E_HIP, std::string("eval launch: ") + hipGetErrorString(e));
+  // the cache holds the sequences, but the model's own logits rows were not
+  // refreshed: a decode step needs a prefill first
+  m->h_lens.clear();
+  m->h_limit.clear();
+  return NGPT_OK;
 }
 
 int ngpt_retire(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, int32_t n) {

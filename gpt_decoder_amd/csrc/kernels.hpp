@@ -123,6 +123,14 @@ void launch_attn_proj(int dtype, const float* part, const int32_t* pos, int H,
                       int hs, int nchunk, int chunk_keys, const void* W, int M,
                       int C, const EpiArgs& e, hipStream_t s);
 
+// Cross-entropy of packed rows against the next id of the same sequence
+// (none for a sequence's last row, whose loss is 0), and the mean over the
+// nscored scored rows.  logits [M][ld] fp32; ids packed [M].
+void launch_cross_entropy(const float* logits, int ld, int V, int M, int nscored,
+                          const int32_t* ids, const int32_t* row_b,
+                          const int32_t* last_rows, float* losses, float* mean,
+                          hipStream_t s);
+
 // Argument pack of the sampler kernel, used to (re)write its graph node.
 struct SamplerArgs {
   int mode = 0;

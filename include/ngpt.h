@@ -287,6 +287,27 @@ int ngpt_slide(ngpt_model *m, ngpt_kv *kv, const int32_t *slots, int32_t n,
                const int32_t *next_ids);
 
 /*
+ * Evaluation forward with labels (model-building chapter "第 4 章 模型构建",
+ * section 4.6: logits at every position; the last position is dropped and
+ * the labels, the ids themselves, are shifted by one; the loss is the mean
+ * cross-entropy).  For B sequences (host ids [B][Tmax], lens[b] in [1,
+ * block_size], sum(lens) <= max_prefill_tokens) the forward runs over every
+ * position from an empty cache (kv holds their K/V afterwards), then ln_f and
+ * the tied lm_head on every row:
+ *   logits     device fp32 [sum(lens)][vocab], packed rows (sequence b's
+ *              rows follow sequence b-1's), output
+ *   losses     device fp32 [sum(lens)], output: row t of a sequence gets
+ *              log(sum_j exp(l_j)) - l[id at t+1]; its last row gets 0
+ *   mean_loss  device fp32 [1], output: the mean over the sum(lens) - B
+ *              scored rows (0 if there are none)
+ * The model's own logits buffer is not refreshed, so decoding needs a new
+ * prefill afterwards.  Errors: as ngpt_prefill.
+ */
+int ngpt_eval_loss(ngpt_model *m, ngpt_kv *kv, const int32_t *ids,
+                   const int32_t *lens, int32_t B, int32_t Tmax, float *logits,
+                   float *losses, float *mean_loss);
+
+/*
  * One decode step for all kv->batch sequences (the loop body of generate()
  * in the serving page, section 2, with the KV cache of its "一个值得做的改进"
  * section: only the newest token is run, against the cached K/V): for every

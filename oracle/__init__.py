@@ -26,8 +26,10 @@ Sources (the pages as a reader has them):
   blocks, a 4x Linear-GELU-Linear MLP, weight tying of wte and lm_head,
   lm_head on the last position only at inference).
 * model-building chapter "第 4 章 模型构建", sections 4.3 (parameter count
-  formula) and 4.5 (token + learned absolute position embeddings, the
-  lower-triangular causal mask, final LayerNorm, bias-free tied lm_head).
+  formula), 4.5 (token + learned absolute position embeddings, the
+  lower-triangular causal mask, final LayerNorm, bias-free tied lm_head) and
+  4.6 (the loss: cross-entropy of every position's logits against the next
+  id, the last position dropped).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, special cases, library routines, brute force, invariants).
@@ -35,13 +37,13 @@ The absolute logits of any *trained* GPT-2 are parity unpinned: the pages
 print no numeric example and no trained weights are available.
 """
 from .gpt import (OracleGPT, layer_norm, gelu, linear, causal_attention,
-                  softmax_rows, round_bf16, count_parameters,
+                  softmax_rows, cross_entropy_rows, round_bf16, count_parameters,
                   param_count_closed_form, param_count_page_estimate)
 from .sampler import sample_rows, sample_row, topk_keep_set
 
 __all__ = [
     "OracleGPT", "layer_norm", "gelu", "linear", "causal_attention",
-    "softmax_rows", "round_bf16", "count_parameters",
+    "softmax_rows", "cross_entropy_rows", "round_bf16", "count_parameters",
     "param_count_closed_form", "param_count_page_estimate",
     "sample_rows", "sample_row", "topk_keep_set",
 ]

@@ -79,6 +79,16 @@ def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
     return y
 
 
+def cross_entropy_rows(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Cross-entropy of each row of logits against its target id:
+    log(sum_j exp(l_j)) - l_target, the log-sum-exp taken around the row
+    maximum.  (Model-building chapter "第 4 章 模型构建", section 4.6: the loss
+    is CrossEntropyLoss over the logits and labels.)"""
+    m = np.max(logits, axis=-1, keepdims=True)
+    lse = m[:, 0] + np.log(np.sum(np.exp(logits - m), axis=-1))
+    return lse - logits[np.arange(len(targets)), targets]
+
+
 def softmax_rows(s: np.ndarray) -> np.ndarray:
     """Softmax over the last axis, max-subtracted; -inf entries give 0."""
     m = np.max(s, axis=-1, keepdims=True)
@@ -325,6 +335,16 @@ class OracleGPT:
         col: dict = {}
         self._forward_rows(np.asarray(ids), cache, collect=col)
         return col.get("x", [])
+
+    def eval_losses(self, ids: Sequence[int]):
+        """The forward with labels of the model-building chapter, section
+        4.6, for one sequence: logits at every position; the last position
+        is dropped and the labels (the ids themselves) are shifted by one, so
+        position t is scored against ids[t + 1].  Returns (logits [T, V],
+        per-position losses [T - 1])."""
+        ids = list(ids)
+        lg = self.full_logits(ids, positions=list(range(len(ids))))
+        return lg, cross_entropy_rows(lg[:-1], np.asarray(ids[1:]))
 
     def window_logits(self, tokens: Sequence[int]) -> np.ndarray:
         """generate()'s crop (serving page, section 2): the logits [V] of

@@ -107,7 +107,6 @@ def test_continuous_batching_admit_and_retire():
     import gpt_decoder_amd as ng
     w = small("bf16", L=2, H=4, C=256, Tb=128, batch=4)
     W = synth.make_weights(w, gamma_std=0.1)
-    W["wte"] = W["wte"] * np.float32(8.0)   # greedy ids that move step to step
     rng = np.random.default_rng(7)
     m = make_model(w, W, max_batch=4, max_prefill_tokens=256)
     m.set_sampling(greedy=True)
@@ -169,7 +168,11 @@ def test_generation_past_block_size(dtype):
     w = synth.Workload(f"crop_{dtype}", 42, 2, 4, 128 if dtype == "f32" else 256, Tb, 97, 97,
                        False, dtype, batch=2, prompt_len=16)
     W = synth.make_weights(w)
-    W["wte"] = W["wte"] * np.float32(8.0)
+    if dtype == "f32":
+        # a larger tied embedding spreads the logits, so that nearly every
+        # greedy id is decided beyond the fp32 tolerance (the bf16 model keeps
+        # the plain init, at which the 2e-2 bar is stated)
+        W["wte"] = W["wte"] * np.float32(8.0)
     rng = np.random.default_rng(8)
     prompts = rng.integers(0, w.vocab_size, (2, 16)).astype(np.int32)
     m = make_model(w, W, max_batch=2, max_prefill_tokens=2 * Tb)

@@ -346,6 +346,37 @@ def test_window_logits_is_the_crop_of_the_last_block():
     np.testing.assert_array_equal(o.window_logits(toks[:10]), o.full_logits(toks[:10])[0])
 
 
+def test_cross_entropy_vs_torch_and_closed_forms():
+    lg = rng.standard_normal((30, 50)) * 4
+    tg = rng.integers(0, 50, 30)
+    want = F.cross_entropy(torch.from_numpy(lg), torch.from_numpy(tg), reduction="none").numpy()
+    np.testing.assert_allclose(oracle.cross_entropy_rows(lg, tg), want, rtol=0, atol=1e-12)
+    # equal logits: log(V); one dominant logit on the target: ~0
+    np.testing.assert_allclose(oracle.cross_entropy_rows(np.zeros((1, 65)), np.array([7])),
+                               [math.log(65)], rtol=1e-15)
+    big = np.zeros((1, 10)); big[0, 3] = 60.0
+    assert 0 <= oracle.cross_entropy_rows(big, np.array([3]))[0] < 1e-24
+    # large offsets do not overflow (the maximum is taken out)
+    np.testing.assert_allclose(oracle.cross_entropy_rows(lg + 1e4, tg), want, atol=1e-9)
+
+
+def test_eval_losses_shift_labels_by_one():
+    """Position t is scored against ids[t+1] with the logits of position t
+    (model-building chapter, section 4.6: logits drop the last position,
+    labels drop the first); brute force over the positions."""
+    cfg = small_cfg(L=2, Tb=32, bias=True)
+    w = synth.make_weights(cfg)
+    ids = list(rng.integers(0, cfg.vocab_size, 12))
+    o = OracleGPT(cfg, w)
+    lg, loss = o.eval_losses(ids)
+    assert lg.shape == (12, cfg.vocab_size) and loss.shape == (11,)
+    for t in range(11):
+        p = np.exp(lg[t] - lg[t].max())
+        p /= p.sum()
+        np.testing.assert_allclose(loss[t], -math.log(p[ids[t + 1]]), rtol=1e-12)
+    np.testing.assert_allclose(lg[5], o.full_logits(ids[:6])[0], rtol=0, atol=1e-12)
+
+
 def test_batch_rows_are_independent_and_ragged():
     cfg = small_cfg(bias=True)
     w = synth.make_weights(cfg)
