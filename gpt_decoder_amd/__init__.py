@@ -8,13 +8,13 @@ from .binding import (workspace_bytes, Config, KVCache, Model, NgptError, check_
                       kv_bytes, lib, make_config, model_from_workload,
                       LIB_PATH, NGPT_OK, NGPT_E_ARG, NGPT_E_CONFIG,
                       NGPT_E_RANGE, NGPT_E_SIZE, NGPT_E_CONTEXT, NGPT_E_HIP,
-                      NGPT_E_DEVICE, NGPT_E_TIMEOUT, NGPT_F32, NGPT_BF16,
+                      NGPT_E_DEVICE, NGPT_E_TIMEOUT, NGPT_F32, NGPT_BF16, NGPT_F16,
                       NGPT_MAX_BATCH)
 
 __all__ = [
     "Config", "KVCache", "Model", "NgptError", "check_config", "kv_bytes",
     "lib", "make_config", "model_from_workload", "LIB_PATH", "NGPT_OK",
     "NGPT_E_ARG", "NGPT_E_CONFIG", "NGPT_E_RANGE", "NGPT_E_SIZE",
-    "NGPT_E_CONTEXT", "NGPT_E_HIP", "NGPT_E_DEVICE", "NGPT_E_TIMEOUT", "NGPT_F32", "NGPT_BF16",
+    "NGPT_E_CONTEXT", "NGPT_E_HIP", "NGPT_E_DEVICE", "NGPT_E_TIMEOUT", "NGPT_F32", "NGPT_BF16", "NGPT_F16",
     "NGPT_MAX_BATCH",
 ]

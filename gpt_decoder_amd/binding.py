@@ -27,6 +27,7 @@ NGPT_E_DEVICE = -7
 NGPT_E_TIMEOUT = -8
 NGPT_F32 = 0
 NGPT_BF16 = 1
+NGPT_F16 = 2
 NGPT_MAX_BATCH = 256
 
 
@@ -132,7 +133,7 @@ def _status_name(code: int) -> str:
 
 def make_config(n_layer, n_head, n_embd, block_size, vocab_size, bias, dtype,
                 max_batch, max_prefill_tokens) -> Config:
-    d = {"f32": NGPT_F32, "bf16": NGPT_BF16}.get(dtype, dtype)
+    d = {"f32": NGPT_F32, "bf16": NGPT_BF16, "f16": NGPT_F16}.get(dtype, dtype)
     return Config(n_layer, n_head, n_embd, block_size, vocab_size, int(bias),
                   d, max_batch, max_prefill_tokens)
 
@@ -188,7 +189,8 @@ class Model:
         self.cfg = make_config(n_layer, n_head, n_embd, block_size, vocab_size,
                                bias, dtype, max_batch, max_prefill_tokens)
         self.vocab = vocab_size
-        tdt = torch.bfloat16 if self.cfg.dtype == NGPT_BF16 else torch.float32
+        tdt = {NGPT_BF16: torch.bfloat16, NGPT_F16: torch.float16}.get(self.cfg.dtype,
+                                                                       torch.float32)
         keep = []
 
         def up(a):

@@ -6,7 +6,9 @@
 namespace ngpt {
 
 typedef uint16_t bf16_t;  // bfloat16 storage: the top 16 bits of an fp32
+typedef _Float16 f16_t;   // IEEE binary16 storage (the fp16 model)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -31,6 +33,11 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
   return f32_to_bf16(x);
 }
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode)
+__device__ __forceinline__ float to_f32(f16_t x) { return static_cast<float>(x); }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) {
+  return static_cast<f16_t>(x);
+}
 
 // Unpack 8 bf16 held in a uint4 (little-endian pairs) to fp32.
 __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float* f) {
@@ -46,6 +53,39 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float* f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_hw_t{a, b}, bf16x2_hw_t));
 }
+
+// Unpack 8 fp16 held in a uint4 (little-endian pairs) to fp32.
+__device__ __forceinline__ void f16x8_to_f32(const uint4 v, float* f) {
+  const f16x8_t h = __builtin_bit_cast(f16x8_t, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<f16_t>(a));
+  const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<f16_t>(b));
+  return lo | (hi << 16);
+}
+
+// The same operations chosen by storage type T (bf16_t or f16_t): 8 values
+// of a 16-byte vector to fp32, two values packed into 32 bits, the MFMA
+// operand vector type and its 16x16x32 MFMA.
+template <class T> struct Half16;
+template <> struct Half16<bf16_t> {
+  typedef bf16x8_t vec8;
+  static __device__ __forceinline__ void unpack8(const uint4 v, float* f) { bf16x8_to_f32(v, f); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ f32x4_t mfma(vec8 a, vec8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Half16<f16_t> {
+  typedef f16x8_t vec8;
+  static __device__ __forceinline__ void unpack8(const uint4 v, float* f) { f16x8_to_f32(v, f); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_f16x2(a, b); }
+  static __device__ __forceinline__ f32x4_t mfma(vec8 a, vec8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // 2^x with the hardware v_exp_f32: the same value as exp2f wherever that is
 // a normal float, 2^-inf = 0; results below 2^-126 (softmax weights too

@@ -226,8 +226,9 @@ static int check_config(const ngpt_config* c, std::string* why) {
   if (c->n_embd % c->n_head != 0) return bad("n_embd % n_head != 0");
   const int hs = c->n_embd / c->n_head;
   if (hs != 32 && hs != 64) return bad("head_dim must be 32 or 64");
-  if (c->dtype != NGPT_F32 && c->dtype != NGPT_BF16) return bad("unknown dtype");
-  if (c->dtype == NGPT_BF16 && c->n_embd % 64 != 0) return bad("bf16 needs n_embd % 64 == 0");
+  if (c->dtype != NGPT_F32 && c->dtype != NGPT_BF16 && c->dtype != NGPT_F16)
+    return bad("unknown dtype");
+  if (c->dtype != NGPT_F32 && c->n_embd % 64 != 0) return bad("bf16 / fp16 need n_embd % 64 == 0");
   if (c->dtype == NGPT_F32 && c->n_embd % 4 != 0) return bad("fp32 needs n_embd % 4 == 0");
   if (c->n_embd > 2048) return bad("n_embd must be <= 2048");
   if (c->block_size < 1 || c->block_size > 4096) return bad("block_size must be in [1, 4096]");
@@ -238,7 +239,7 @@ static int check_config(const ngpt_config* c, std::string* why) {
   // The kernels address each matrix with 32-bit buffer offsets and use
   // offset 2^31 as "past the end" (reads zeros), so every weight matrix and
   // every activation buffer must stay below 2 GiB.
-  const size_t esz = c->dtype == NGPT_BF16 ? 2 : 4;
+  const size_t esz = c->dtype == NGPT_F32 ? 4 : 2;
   const size_t kMaxBytes = (size_t)1 << 31;
   if ((size_t)c->vocab_size * c->n_embd * esz >= kMaxBytes)
     return bad("vocab_size * n_embd too large (the embedding matrix must be < 2 GiB)");
@@ -267,7 +268,7 @@ int ngpt_check_config(const ngpt_config* cfg) {
 
 size_t ngpt_kv_bytes(const ngpt_config* cfg, int32_t batch) {
   if (check_config(cfg, nullptr) != NGPT_OK || batch < 1) return 0;
-  const size_t es = cfg->dtype == NGPT_BF16 ? 2 : 4;
+  const size_t es = cfg->dtype == NGPT_F32 ? 4 : 2;
   return (size_t)cfg->n_layer * batch * cfg->n_head * cfg->block_size *
          (cfg->n_embd / cfg->n_head) * es;
 }
@@ -281,7 +282,7 @@ static WsLayout ws_layout(const ngpt_config* cfg) {
   WsLayout o;
   const size_t Mm = std::max(cfg->max_prefill_tokens, cfg->max_batch);
   const size_t Bm = cfg->max_batch, C = cfg->n_embd;
-  const size_t es = cfg->dtype == NGPT_BF16 ? 2 : 4;
+  const size_t es = cfg->dtype == NGPT_F32 ? 4 : 2;
   const int H = cfg->n_head, hs = cfg->n_embd / cfg->n_head, Tb = cfg->block_size;
   const int nchunk = attn_decode_chunks(Tb);
   size_t off = 0;
@@ -357,7 +358,7 @@ static int create_on(const ngpt_config* cfg, const ngpt_weights* w, void* ws,
   m->cfg = *cfg;
   m->L = cfg->n_layer; m->H = cfg->n_head; m->C = cfg->n_embd;
   m->hs = m->C / m->H; m->Tb = cfg->block_size; m->V = cfg->vocab_size;
-  m->esz = cfg->dtype == NGPT_BF16 ? 2 : 4;
+  m->esz = cfg->dtype == NGPT_F32 ? 4 : 2;
   m->Mmax = std::max(cfg->max_prefill_tokens, cfg->max_batch);
   m->nchunk = attn_decode_chunks(m->Tb);
   m->wte = w->wte; m->wpe = w->wpe; m->lnf_w = w->lnf_w; m->lnf_b = w->lnf_b;

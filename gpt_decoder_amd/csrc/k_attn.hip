@@ -13,7 +13,7 @@
 // is a contiguous [Tb][hs] block.
 //
 // Kernels:
-//   attn_prefill_mfma   bf16, one workgroup per (64-row query tile, head,
+//   attn_prefill_mfma   bf16 / fp16, one workgroup per (64-row query tile, head,
 //                       sequence); K/V tiles of 64 keys staged in LDS;
 //                       scores and P*V on MFMA; online (running max / sum)
 //                       softmax in fp32; tiles above the diagonal skipped.
@@ -49,11 +49,12 @@ constexpr int kPrefillKch = 4;   // key tiles per chunk when a prefill tile is s
 // chunk leaves its rows' unnormalised state (m, l, o) in part, and
 // attn_prefill_merge combines the chunks in order.  Workgroup x takes query
 // tile ntiles - 1 - x / nsplit (heavy tiles first) and chunk x % nsplit.
-template <int HS>
+template <class T, int HS>
 __global__ __launch_bounds__(256) void attn_prefill_mfma(
-    const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc,
-    const bf16_t* __restrict__ vc, RowMap map, int H, int Tb, float scale,
-    bf16_t* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part) {
+    const T* __restrict__ q, int ldq, const T* __restrict__ kc,
+    const T* __restrict__ vc, RowMap map, int H, int Tb, float scale,
+    T* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part) {
+  typedef typename Half16<T>::vec8 vec8;
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = HS + 8;         // sK row stride (elements)
   constexpr int VS = KT + 8;         // sVt row stride (elements)
@@ -83,17 +84,17 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const int kend = past + len;                    // keys in the cache
   const size_t row0 = (size_t)map.off[b];
   const int slot = map.slot[b];
-  const bf16_t* kbase = kc + ((size_t)slot * H + h) * Tb * HS;
-  const bf16_t* vbase = vc + ((size_t)slot * H + h) * Tb * HS;
+  const T* kbase = kc + ((size_t)slot * H + h) * Tb * HS;
+  const T* vbase = vc + ((size_t)slot * H + h) * Tb * HS;
 
   // Q^T operand: column = this lane's query, K-values = dims 8g.. (+32 kk)
-  bf16x8_t qf[NKK];
+  vec8 qf[NKK];
   {
     const int qr = qrow < len ? qrow : len - 1;
-    const bf16_t* qp = q + (row0 + qr) * ldq + h * HS;
+    const T* qp = q + (row0 + qr) * ldq + h * HS;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 32 + g * 8);
+      qf[kk] = *reinterpret_cast<const vec8*>(qp + kk * 32 + g * 8);
   }
 
   const float sl2 = scale * kLog2e;
@@ -114,9 +115,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   constexpr uint32_t kOut = 0x80000000u;
   const uint32_t blk = (uint32_t)Tb * HS * 2u;
   const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(kbase), (short)0, (int)blk, 0x00020000);
+      const_cast<T*>(kbase), (short)0, (int)blk, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(vbase), (short)0, (int)blk, 0x00020000);
+      const_cast<T*>(vbase), (short)0, (int)blk, 0x00020000);
   uint4 rk[S][IPT][2], rv[S][IPT][2];
   auto load_tile = [&](int st, int k0) {
 #pragma unroll
@@ -171,9 +172,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+        const vec8 kf = *reinterpret_cast<const vec8*>(
             sK + (t * 16 + (lane & 15)) * KS + kk * 32 + g * 8);
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[t], 0, 0, 0);
+        s[t] = Half16<T>::mfma(kf, qf[kk], s[t]);
       }
     }
     // mask and tile maximum (log2 domain)
@@ -210,22 +211,21 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     // O^T += V^T P^T, 32 keys per MFMA: sub-tiles 2u and 2u+1
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8_t pf;
+      vec8 pf;
       {
-        const uint32_t w0 = pack_bf16x2(s[2 * u][0], s[2 * u][1]);
-        const uint32_t w1 = pack_bf16x2(s[2 * u][2], s[2 * u][3]);
-        const uint32_t w2 = pack_bf16x2(s[2 * u + 1][0], s[2 * u + 1][1]);
-        const uint32_t w3 = pack_bf16x2(s[2 * u + 1][2], s[2 * u + 1][3]);
-        pf = __builtin_bit_cast(bf16x8_t, make_uint4(w0, w1, w2, w3));
+        const uint32_t w0 = Half16<T>::pack2(s[2 * u][0], s[2 * u][1]);
+        const uint32_t w1 = Half16<T>::pack2(s[2 * u][2], s[2 * u][3]);
+        const uint32_t w2 = Half16<T>::pack2(s[2 * u + 1][0], s[2 * u + 1][1]);
+        const uint32_t w3 = Half16<T>::pack2(s[2 * u + 1][2], s[2 * u + 1][3]);
+        pf = __builtin_bit_cast(vec8, make_uint4(w0, w1, w2, w3));
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const bf16_t* vr = sVt + (d * 16 + (lane & 15)) * VS + u * 32 + g * 4;
         const uint2 lo = *reinterpret_cast<const uint2*>(vr);
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        const bf16x8_t vf =
-            __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[d], 0, 0, 0);
+        const vec8 vf = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[d] = Half16<T>::mfma(vf, pf, o[d]);
       }
     }
   }
@@ -245,11 +245,11 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   }
   if (qrow < len) {
     const float inv = 1.f / l_run;
-    bf16_t* yp = y + (row0 + qrow) * ldy + h * HS;
+    T* yp = y + (row0 + qrow) * ldy + h * HS;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      const uint32_t w0 = pack_bf16x2(o[d][0] * inv, o[d][1] * inv);
-      const uint32_t w1 = pack_bf16x2(o[d][2] * inv, o[d][3] * inv);
+      const uint32_t w0 = Half16<T>::pack2(o[d][0] * inv, o[d][1] * inv);
+      const uint32_t w1 = Half16<T>::pack2(o[d][2] * inv, o[d][3] * inv);
       *reinterpret_cast<uint2*>(yp + d * 16 + g * 4) = make_uint2(w0, w1);
     }
   }
@@ -259,10 +259,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 // head), four rows per workgroup; lane d merges dimension d over the chunks
 // in chunk order.  Rows whose tile had a single chunk were written directly.
 constexpr int kMergeRows = 4;
-template <int HS>
+template <class T, int HS>
 __global__ __launch_bounds__(64 * kMergeRows) void attn_prefill_merge(
     const float* __restrict__ part, int len, int past, int Tb, int kch, int nsplit,
-    bf16_t* __restrict__ y, int ldy, int r0) {
+    T* __restrict__ y, int ldy, int r0) {
   const int row = r0 + (int)blockIdx.x * kMergeRows + (int)(threadIdx.x >> 6);
   const int h = blockIdx.y, d = threadIdx.x & 63;
   if (row >= len || d >= HS) return;
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_prefill_merge(
     const float* pc = pp + c * (HS + 4);
     merge_state(m, l, &o, pc[0], pc[1], &pc[4 + d], 1);
   }
-  y[(size_t)row * ldy + h * HS + d] = f32_to_bf16(o / l);
+  y[(size_t)row * ldy + h * HS + d] = from_f32<T>(o / l);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int u = kw + pass * KPP + kgrp;
     if (u <= p) {
       if constexpr (sizeof(T) == 2) {
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kbase + (size_t)u * HS + sub * 8), kf[pass]);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(vbase + (size_t)u * HS + sub * 8), vf[pass]);
+        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(kbase + (size_t)u * HS + sub * 8), kf[pass]);
+        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(vbase + (size_t)u * HS + sub * 8), vf[pass]);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -471,43 +471,53 @@ __global__ __launch_bounds__(64) void attn_decode_combine(
 // ---------------------------------------------------------------------------
 int attn_prefill_split_chunks(int Tb) { return ((Tb + 63) / 64 + kPrefillKch - 1) / kPrefillKch; }
 
+template <class T>
+static void launch_attn_prefill_h(const T* q, int ldq, const T* kc, const T* vc,
+                                  const RowMap& map, int maxlen, int H, int hs, int Tb,
+                                  T* y, int ldy, float* part, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)hs);
+  const int ntiles = (maxlen + 63) / 64;
+  // one sequence with few workgroups: split the long query tiles' keys
+  const int past = map.past[0];
+  const int nkt_max = (past + maxlen - 1) / 64 + 1;
+  const bool split = part && map.B == 1 && nkt_max > kPrefillKch && ntiles * H < 256;
+  const int kch = split ? kPrefillKch : 0;
+  const int nsplit = split ? (nkt_max + kPrefillKch - 1) / kPrefillKch : 1;
+  const dim3 grid(ntiles * nsplit, H, map.B);
+  if (hs == 64)
+    attn_prefill_mfma<T, 64><<<grid, 256, 0, s>>>(q, ldq, kc, vc, map, H, Tb, scale, y, ldy,
+                                                   kch, nsplit, part);
+  else
+    attn_prefill_mfma<T, 32><<<grid, 256, 0, s>>>(q, ldq, kc, vc, map, H, Tb, scale, y, ldy,
+                                                   kch, nsplit, part);
+  if (split) {
+    // rows of single-chunk tiles need no merge: start at the first tile
+    // with more than one chunk
+    int first = 0;
+    while (first < ntiles && (past + min(first * 64 + 63, maxlen - 1)) / 64 + 1 <= kch) ++first;
+    const int r0 = first * 64;
+    const dim3 mgrid((maxlen - r0 + kMergeRows - 1) / kMergeRows, H);
+    if (hs == 64)
+      attn_prefill_merge<T, 64><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, past, Tb, kch,
+                                                                  nsplit, y, ldy, r0);
+    else
+      attn_prefill_merge<T, 32><<<mgrid, 64 * kMergeRows, 0, s>>>(part, maxlen, past, Tb, kch,
+                                                                  nsplit, y, ldy, r0);
+  }
+}
+
 void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
                          const void* vc, const RowMap& map, int maxlen, int H,
                          int hs, int Tb, void* y, int ldy, float* part, hipStream_t s) {
-  const float scale = 1.0f / sqrtf((float)hs);
-  const int ntiles = (maxlen + 63) / 64;
   if (dtype == NGPT_BF16) {
-    const bf16_t* qq = (const bf16_t*)q;
-    // one sequence with few workgroups: split the long query tiles' keys
-    const int past = map.past[0];
-    const int nkt_max = (past + maxlen - 1) / 64 + 1;
-    const bool split = part && map.B == 1 && nkt_max > kPrefillKch && ntiles * H < 256;
-    const int kch = split ? kPrefillKch : 0;
-    const int nsplit = split ? (nkt_max + kPrefillKch - 1) / kPrefillKch : 1;
-    const dim3 grid(ntiles * nsplit, H, map.B);
-    if (hs == 64)
-      attn_prefill_mfma<64><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
-          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
-    else
-      attn_prefill_mfma<32><<<grid, 256, 0, s>>>(qq, ldq, (const bf16_t*)kc,
-          (const bf16_t*)vc, map, H, Tb, scale, (bf16_t*)y, ldy, kch, nsplit, part);
-    if (split) {
-      // rows of single-chunk tiles need no merge: start at the first tile
-      // with more than one chunk
-      int first = 0;
-      while (first < ntiles && (past + min(first * 64 + 63, maxlen - 1)) / 64 + 1 <= kch) ++first;
-      const int r0 = first * 64;
-      const dim3 mgrid((maxlen - r0 + kMergeRows - 1) / kMergeRows, H);
-      const float* pp = part;
-      bf16_t* yy = (bf16_t*)y;
-      if (hs == 64)
-        attn_prefill_merge<64><<<mgrid, 64 * kMergeRows, 0, s>>>(pp, maxlen, past, Tb, kch, nsplit,
-                                                                yy, ldy, r0);
-      else
-        attn_prefill_merge<32><<<mgrid, 64 * kMergeRows, 0, s>>>(pp, maxlen, past, Tb, kch, nsplit,
-                                                                yy, ldy, r0);
-    }
+    launch_attn_prefill_h<bf16_t>((const bf16_t*)q, ldq, (const bf16_t*)kc, (const bf16_t*)vc,
+                                  map, maxlen, H, hs, Tb, (bf16_t*)y, ldy, part, s);
+  } else if (dtype == NGPT_F16) {
+    launch_attn_prefill_h<f16_t>((const f16_t*)q, ldq, (const f16_t*)kc, (const f16_t*)vc,
+                                 map, maxlen, H, hs, Tb, (f16_t*)y, ldy, part, s);
   } else {
+    const float scale = 1.0f / sqrtf((float)hs);
+    const int ntiles = (maxlen + 63) / 64;
     const dim3 grid(ntiles, H, map.B);
     const float* qq = (const float*)q;
     if (hs == 64)
@@ -523,33 +533,35 @@ int attn_decode_chunks(int Tb) { return (Tb + kDecChunk - 1) / kDecChunk; }
 
 int attn_decode_chunk_keys() { return kDecChunk; }
 
+template <class T>
+static void launch_attn_decode_t(const T* q, const T* kc, const T* vc, const int32_t* pos,
+                                 int B, int H, int hs, int Tb, float* part, T* y,
+                                 bool merge_into_y, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)hs);
+  const int nchunk = attn_decode_chunks(Tb);
+  const dim3 grid(nchunk, H, B), cgrid(H, B);
+  if (hs == 64) {
+    attn_decode_kernel<T, 64><<<grid, 256, 0, s>>>(q, kc, vc, pos, H, Tb, nchunk, scale, part);
+    if (merge_into_y) attn_decode_combine<T, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, y);
+  } else {
+    attn_decode_kernel<T, 32><<<grid, 256, 0, s>>>(q, kc, vc, pos, H, Tb, nchunk, scale, part);
+    if (merge_into_y) attn_decode_combine<T, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, y);
+  }
+}
+
 void launch_attn_decode(int dtype, const void* q, const void* kc,
                         const void* vc, const int32_t* pos, int B, int H,
                         int hs, int Tb, float* part, void* y,
                         bool merge_into_y, hipStream_t s) {
-  const float scale = 1.0f / sqrtf((float)hs);
-  const int nchunk = attn_decode_chunks(Tb);
-  const dim3 grid(nchunk, H, B), cgrid(H, B);
   if (dtype == NGPT_BF16) {
-    if (hs == 64) {
-      attn_decode_kernel<bf16_t, 64><<<grid, 256, 0, s>>>((const bf16_t*)q,
-          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part);
-      if (merge_into_y) attn_decode_combine<bf16_t, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (bf16_t*)y);
-    } else {
-      attn_decode_kernel<bf16_t, 32><<<grid, 256, 0, s>>>((const bf16_t*)q,
-          (const bf16_t*)kc, (const bf16_t*)vc, pos, H, Tb, nchunk, scale, part);
-      if (merge_into_y) attn_decode_combine<bf16_t, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (bf16_t*)y);
-    }
+    launch_attn_decode_t<bf16_t>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, pos,
+                                 B, H, hs, Tb, part, (bf16_t*)y, merge_into_y, s);
+  } else if (dtype == NGPT_F16) {
+    launch_attn_decode_t<f16_t>((const f16_t*)q, (const f16_t*)kc, (const f16_t*)vc, pos,
+                                B, H, hs, Tb, part, (f16_t*)y, merge_into_y, s);
   } else {
-    if (hs == 64) {
-      attn_decode_kernel<float, 64><<<grid, 256, 0, s>>>((const float*)q,
-          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part);
-      if (merge_into_y) attn_decode_combine<float, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (float*)y);
-    } else {
-      attn_decode_kernel<float, 32><<<grid, 256, 0, s>>>((const float*)q,
-          (const float*)kc, (const float*)vc, pos, H, Tb, nchunk, scale, part);
-      if (merge_into_y) attn_decode_combine<float, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, (float*)y);
-    }
+    launch_attn_decode_t<float>((const float*)q, (const float*)kc, (const float*)vc, pos,
+                                B, H, hs, Tb, part, (float*)y, merge_into_y, s);
   }
 }
 

@@ -89,12 +89,22 @@ __device__ __forceinline__ void load4(const bf16_t* p, float* f) {
   f[2] = to_f32(static_cast<bf16_t>(u.y & 0xffffu));
   f[3] = to_f32(static_cast<bf16_t>(u.y >> 16));
 }
+__device__ __forceinline__ void load4(const f16_t* p, float* f) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  f[0] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.x & 0xffffu)));
+  f[1] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.x >> 16)));
+  f[2] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.y & 0xffffu)));
+  f[3] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.y >> 16)));
+}
 __device__ __forceinline__ void load4(const float* p, float* f) {
   const float4 t = *reinterpret_cast<const float4*>(p);
   f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
 }
 __device__ __forceinline__ void store4(bf16_t* p, const float* f) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+}
+__device__ __forceinline__ void store4(f16_t* p, const float* f) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]));
 }
 __device__ __forceinline__ void store4(float* p, const float* f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
@@ -160,6 +170,10 @@ void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
     embed_prefill_kernel<bf16_t><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const bf16_t*)wte, (const bf16_t*)wpe, C, V, x,
         row_b, row_pos, last_rows, last_slot, hist, Tb, status);
+  else if (dtype == NGPT_F16)
+    embed_prefill_kernel<f16_t><<<M, 256, 0, s>>>(
+        ids, Tmax, map, (const f16_t*)wte, (const f16_t*)wpe, C, V, x,
+        row_b, row_pos, last_rows, last_slot, hist, Tb, status);
   else
     embed_prefill_kernel<float><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const float*)wte, (const float*)wpe, C, V, x, row_b,
@@ -172,6 +186,9 @@ void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,
   if (dtype == NGPT_BF16)
     embed_decode_kernel<bf16_t><<<B, 256, 0, s>>>(
         tok, pos, (const bf16_t*)wte, (const bf16_t*)wpe, C, V, x, status);
+  else if (dtype == NGPT_F16)
+    embed_decode_kernel<f16_t><<<B, 256, 0, s>>>(
+        tok, pos, (const f16_t*)wte, (const f16_t*)wpe, C, V, x, status);
   else
     embed_decode_kernel<float><<<B, 256, 0, s>>>(
         tok, pos, (const float*)wte, (const float*)wpe, C, V, x, status);
@@ -186,6 +203,9 @@ void launch_layernorm(int dtype, const float* x, int ldx, const int32_t* rows,
     layernorm_kernel<bf16_t><<<grid, 256, 0, s>>>(
         x, ldx, rows, M, (const bf16_t*)w, (const bf16_t*)b, (bf16_t*)out, ldo,
         C);
+  else if (dtype == NGPT_F16)
+    layernorm_kernel<f16_t><<<grid, 256, 0, s>>>(
+        x, ldx, rows, M, (const f16_t*)w, (const f16_t*)b, (f16_t*)out, ldo, C);
   else
     layernorm_kernel<float><<<grid, 256, 0, s>>>(
         x, ldx, rows, M, (const float*)w, (const float*)b, (float*)out, ldo, C);

@@ -57,16 +57,26 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
   }
 }
 
+// A 16-bit element from its bit pattern.
+template <class T> __device__ __forceinline__ float bits_to_f32(uint32_t u16);
+template <> __device__ __forceinline__ float bits_to_f32<bf16_t>(uint32_t u16) {
+  return to_f32(static_cast<bf16_t>(u16));
+}
+template <> __device__ __forceinline__ float bits_to_f32<f16_t>(uint32_t u16) {
+  return to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u16)));
+}
+
 // Bias of four consecutive output columns col .. col + 3 (the MFMA kernel's
-// bf16 epilogues), by value so that nothing goes to scratch; columns at or
+// 16-bit epilogues), by value so that nothing goes to scratch; columns at or
 // past N get none.
-__device__ __forceinline__ float4 add_bias4(const bf16_t* b, int col, int N, float4 v) {
+template <class T>
+__device__ __forceinline__ float4 add_bias4(const T* b, int col, int N, float4 v) {
   if (col + 3 < N) {
     const uint2 u = *reinterpret_cast<const uint2*>(b + col);
-    v.x += to_f32(static_cast<bf16_t>(u.x & 0xffffu));
-    v.y += to_f32(static_cast<bf16_t>(u.x >> 16));
-    v.z += to_f32(static_cast<bf16_t>(u.y & 0xffffu));
-    v.w += to_f32(static_cast<bf16_t>(u.y >> 16));
+    v.x += bits_to_f32<T>(u.x & 0xffffu);
+    v.y += bits_to_f32<T>(u.x >> 16);
+    v.z += bits_to_f32<T>(u.y & 0xffffu);
+    v.w += bits_to_f32<T>(u.y >> 16);
   } else {
     v.x += to_f32(b[col]);
     if (col + 1 < N) v.y += to_f32(b[col + 1]);
@@ -75,12 +85,15 @@ __device__ __forceinline__ float4 add_bias4(const bf16_t* b, int col, int N, flo
   return v;
 }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
-  return make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+template <class T>
+__device__ __forceinline__ uint2 pack4(float4 v) {
+  return make_uint2(Half16<T>::pack2(v.x, v.y), Half16<T>::pack2(v.z, v.w));
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA tile GEMM.  256 threads = 4 wavefronts in a 2x2 arrangement; each
+// 16-bit MFMA tile GEMM (bf16 or fp16 operands, fp32 accumulation; the
+// v_mfma_f32_16x16x32 bf16 / f16 instruction of the operand type).  256
+// threads = 4 wavefronts in a 2x2 arrangement; each
 // wavefront owns a (BM/2) x (BN/2) sub-tile built from 16x16 MFMA tiles.  K is
 // consumed 64 at a time through a two-stage LDS ring: the next K-slab is
 // fetched into registers while the current one is multiplied, then written
@@ -103,10 +116,11 @@ __device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
 // read-modify-write of the residual).  Both operands are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int EPI, int S, int NKC = 0>
+template <class T, int BM, int BN, int EPI, int S, int NKC = 0>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
-    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int M,
+    const T* __restrict__ A, int lda, const T* __restrict__ W, int M,
     int N, int K, EpiArgs e) {
+  typedef typename Half16<T>::vec8 vec8;
   constexpr int BK = 64;
   constexpr int LDS = BK + 8;  // padded row stride (elements)
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -140,9 +154,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   // zeros, and every load is issued on every path, so the wait before a
   // stage is used covers exactly that stage.
   const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(A), (short)0, (int)((uint32_t)M * (uint32_t)lda * 2u), 0x00020000);
+      const_cast<T*>(A), (short)0, (int)((uint32_t)M * (uint32_t)lda * 2u), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * 2u), 0x00020000);
+      const_cast<T*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * 2u), 0x00020000);
   auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   };
@@ -231,25 +245,23 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
       gload(st, (it + S) * BK);
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 32) {
-        bf16x8_t af[TM], bfr[TN];
+        vec8 af[TM], bfr[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int r = wm * WM + i * 16 + (lane & 15);
-          af[i] = *reinterpret_cast<const bf16x8_t*>(sA[buf] + r * LDS + kk + (lane >> 4) * 8);
+          af[i] = *reinterpret_cast<const vec8*>(sA[buf] + r * LDS + kk + (lane >> 4) * 8);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int r = wn * WN + j * 16 + (lane & 15);
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB[buf] + r * LDS + kk + (lane >> 4) * 8);
+          bfr[j] = *reinterpret_cast<const vec8*>(sB[buf] + r * LDS + kk + (lane >> 4) * 8);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = kSwap ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i],
-                                                                        acc[i][j], 0, 0, 0)
-                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
-                                                                        acc[i][j], 0, 0, 0);
+            acc[i][j] = kSwap ? Half16<T>::mfma(bfr[j], af[i], acc[i][j])
+                              : Half16<T>::mfma(af[i], bfr[j], acc[i][j]);
       }
     }
   }
@@ -264,23 +276,23 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
       const int which = col / e.C;
       const int c = col - which * e.C;
       const int hh = c / e.hs, d = c - hh * e.hs;
-      bf16_t* cache = static_cast<bf16_t*>(which == 1 ? e.kc : e.vc);
+      T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = out_row(i);
         if (row >= M) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (e.bias) v = add_bias4(static_cast<const bf16_t*>(e.bias), col, N, v);
-        const uint2 packed = pack_bf16x4(v);
+        if (e.bias) v = add_bias4(static_cast<const T*>(e.bias), col, N, v);
+        const uint2 packed = pack4<T>(v);
         if (which == 0) {
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(e.out) + (size_t)row * e.ldo + c) = packed;
+          *reinterpret_cast<uint2*>(static_cast<T*>(e.out) + (size_t)row * e.ldo + c) = packed;
         } else if (rpos[i] >= 0) {
           *reinterpret_cast<uint2*>(
               cache + (((size_t)rseq[i] * e.H + hh) * e.Tb + rpos[i]) * e.hs + d) = packed;
         }
       }
     }
-  } else if constexpr (kSwap) {  // EPI_GELU: bf16 rows
+  } else if constexpr (kSwap) {  // EPI_GELU: 16-bit rows
     const bool vec = (e.ldo & 3) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -289,16 +301,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         const int row = out_row(i), col = out_col(j);
         if (row >= M || col >= N) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (e.bias) v = add_bias4(static_cast<const bf16_t*>(e.bias), col, N, v);
+        if (e.bias) v = add_bias4(static_cast<const T*>(e.bias), col, N, v);
         v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
-        bf16_t* o = static_cast<bf16_t*>(e.out) + (size_t)row * e.ldo + col;
+        T* o = static_cast<T*>(e.out) + (size_t)row * e.ldo + col;
         if (vec && col + 3 < N) {
-          *reinterpret_cast<uint2*>(o) = pack_bf16x4(v);
+          *reinterpret_cast<uint2*>(o) = pack4<T>(v);
         } else {
-          o[0] = f32_to_bf16(v.x);
-          if (col + 1 < N) o[1] = f32_to_bf16(v.y);
-          if (col + 2 < N) o[2] = f32_to_bf16(v.z);
-          if (col + 3 < N) o[3] = f32_to_bf16(v.w);
+          o[0] = from_f32<T>(v.x);
+          if (col + 1 < N) o[1] = from_f32<T>(v.y);
+          if (col + 2 < N) o[2] = from_f32<T>(v.z);
+          if (col + 3 < N) o[3] = from_f32<T>(v.w);
         }
       }
   } else {
@@ -314,10 +326,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
           if (row >= M) continue;
           if constexpr (kPreRes) {
             float val = acc[i][j][v];
-            if (e.bias) val += to_f32(static_cast<const bf16_t*>(e.bias)[col]);
+            if (e.bias) val += to_f32(static_cast<const T*>(e.bias)[col]);
             static_cast<float*>(e.out)[(size_t)row * e.ldo + col] = res[i][j][v] + val;
           } else {
-            epi_apply<bf16_t, EPI>(e, row, col, acc[i][j][v]);
+            epi_apply<T, EPI>(e, row, col, acc[i][j][v]);
           }
         }
       }
@@ -363,6 +375,9 @@ __device__ __forceinline__ float wave_reduce_multi(float* v) {
 
 __device__ __forceinline__ void load_vec(const bf16_t* p, float* f) {
   bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
+}
+__device__ __forceinline__ void load_vec(const f16_t* p, float* f) {
+  f16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
 }
 __device__ __forceinline__ void load_vec(const float* p, float* f) {
   const float4 t = *reinterpret_cast<const float4*>(p);
@@ -478,7 +493,7 @@ __global__ __launch_bounds__(64) void gemv_kernel(
     for (int c = 0; c < CPW; ++c) {
       float wf[VE];
       if constexpr (sizeof(T) == 2) {
-        bf16x8_to_f32(wv[j][c], wf);
+        Half16<T>::unpack8(wv[j][c], wf);
       } else {
         wf[0] = __uint_as_float(wv[j][c].x);
         wf[1] = __uint_as_float(wv[j][c].y);
@@ -492,7 +507,7 @@ __global__ __launch_bounds__(64) void gemv_kernel(
 #pragma unroll
           for (int q = 0; q < VE; ++q) af[q] = av[m][j][q];
         } else if constexpr (sizeof(T) == 2) {
-          bf16x8_to_f32(araw[m][j], af);
+          Half16<T>::unpack8(araw[m][j], af);
         } else {
           af[0] = __uint_as_float(araw[m][j].x);
           af[1] = __uint_as_float(araw[m][j].y);
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(256) void attn_proj_kernel(
     for (int c = 0; c < CPW; ++c) {
       float wf[VE];
       if constexpr (sizeof(T) == 2) {
-        bf16x8_to_f32(wv[j][c], wf);
+        Half16<T>::unpack8(wv[j][c], wf);
       } else {
         wf[0] = __uint_as_float(wv[j][c].x);
         wf[1] = __uint_as_float(wv[j][c].y);
@@ -647,6 +662,10 @@ void launch_attn_proj(int dtype, const float* part, const int32_t* pos, int H,
     const bf16_t* w = static_cast<const bf16_t*>(W);
     if (hs == 64) launch_attn_proj_h<bf16_t, 64>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
     else launch_attn_proj_h<bf16_t, 32>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+  } else if (dtype == NGPT_F16) {
+    const f16_t* w = static_cast<const f16_t*>(W);
+    if (hs == 64) launch_attn_proj_h<f16_t, 64>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
+    else launch_attn_proj_h<f16_t, 32>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
   } else {
     const float* w = static_cast<const float*>(W);
     if (hs == 64) launch_attn_proj_h<float, 64>(part, pos, H, nchunk, chunk_keys, w, M, C, C, e, s);
@@ -727,26 +746,85 @@ static void gemv_rows(const T* A, int lda, const LnArgs& ln, const T* W, int M,
 }
 
 
+// 16-bit MFMA tile GEMM: tile shape and K-slab staging chosen per shape.
+template <class T, int EPI>
+static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
+                          const EpiArgs& e, hipStream_t s) {
+  // Tile size: a workgroup's time is set by the operand bytes it streams,
+  // (BM + BN) * K, and the grid runs in rounds of one workgroup per CU;
+  // pick the smaller rounds * (BM + BN), 128x64 on a tie.
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  auto cost = [&](int bm, int bn) {
+    constexpr int kCUs = 256;
+    return ((tiles(bm, bn) + kCUs - 1) / kCUs) * (bm + bn);
+  };
+  // K-slab counts of the GPT-2-small widths (768 and 4 * 768) are
+  // compile-time constants, so the K loop is fully unrolled: at every trip
+  // of a rolled loop the compiler waits for all loads in flight.
+  const bool big = M > 64 && cost(128, 64) <= cost(64, 64);
+  // 128x96 tiles for c_attn and c_fc when they cost less (at 1024 rows of
+  // GPT-2 small: 192 and 256 tiles, one round; measured 2-2.5 us faster
+  // per launch than 128x64)
+  constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU;
+  const bool wide = kWideEpi && M > 64 && cost(128, 96) < cost(big ? 128 : 64, 64);
+  const int g = wide ? tiles(128, 96) : big ? tiles(128, 64) : tiles(64, 64);
+  // (only the pairs a block issues: c_attn, c_fc, c_proj at K = 768, the
+  // MLP projection at K = 3072)
+  constexpr bool k768 = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr bool k3072 = EPI == EPI_RESID;
+  bool done = false;
+  if constexpr (k768) {
+    if (K == 768) {
+      if constexpr (kWideEpi) {
+        if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 2, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      }
+      if (!wide) {
+        if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<T, 64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      }
+      done = true;
+    }
+  }
+  if constexpr (k3072) {
+    if (K == 3072) {
+      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      done = true;
+    }
+  }
+  if (!done) {
+    if constexpr (kWideEpi) {
+      if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+    }
+    if (!wide) {
+      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+    }
+  }
+}
+
+template <class T, int EPI>
+static void dispatch_gemv(const void* A, int lda, const LnArgs* ln, const void* W,
+                          int M, int N, int K, const EpiArgs& e, hipStream_t s) {
+  const LnArgs none{};
+  const T* a = static_cast<const T*>(A);
+  const T* w = static_cast<const T*>(W);
+  if (ln) gemv_rows<T, EPI, true>(a, lda, *ln, w, M, N, K, e, s);
+  else gemv_rows<T, EPI, false>(a, lda, none, w, M, N, K, e, s);
+}
+
 template <int EPI>
 static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
                      const void* W, int M, int N, int K, const EpiArgs& e,
                      hipStream_t s) {
-  const LnArgs none{};
   // streaming path: up to 16 chunks of 64 16-byte vectors per row (K <= 8192
-  // bf16 / 4096 fp32), with a fused LayerNorm only up to kGemvLnMaxK
-  const int gemv_max_k = 16 * 64 * (dtype == NGPT_BF16 ? 8 : 4);
+  // 16-bit / 4096 fp32), with a fused LayerNorm only up to kGemvLnMaxK
+  const bool half = dtype == NGPT_BF16 || dtype == NGPT_F16;
+  const int gemv_max_k = 16 * 64 * (half ? 8 : 4);
   if (M <= kGemvMaxRows && K <= gemv_max_k && (!ln || K <= kGemvLnMaxK)) {
-    if (dtype == NGPT_BF16) {
-      const bf16_t* a = static_cast<const bf16_t*>(A);
-      const bf16_t* w = static_cast<const bf16_t*>(W);
-      if (ln) gemv_rows<bf16_t, EPI, true>(a, lda, *ln, w, M, N, K, e, s);
-      else gemv_rows<bf16_t, EPI, false>(a, lda, none, w, M, N, K, e, s);
-    } else {
-      const float* a = static_cast<const float*>(A);
-      const float* w = static_cast<const float*>(W);
-      if (ln) gemv_rows<float, EPI, true>(a, lda, *ln, w, M, N, K, e, s);
-      else gemv_rows<float, EPI, false>(a, lda, none, w, M, N, K, e, s);
-    }
+    if (dtype == NGPT_BF16) dispatch_gemv<bf16_t, EPI>(A, lda, ln, W, M, N, K, e, s);
+    else if (dtype == NGPT_F16) dispatch_gemv<f16_t, EPI>(A, lda, ln, W, M, N, K, e, s);
+    else dispatch_gemv<float, EPI>(A, lda, ln, W, M, N, K, e, s);
     return;
   }
   if (ln) {  // tiled paths read a materialised LayerNorm output
@@ -755,59 +833,11 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
     lda = K;
   }
   if (dtype == NGPT_BF16) {
-    const bf16_t* a = static_cast<const bf16_t*>(A);
-    const bf16_t* w = static_cast<const bf16_t*>(W);
-    // Tile size: a workgroup's time is set by the operand bytes it streams,
-    // (BM + BN) * K, and the grid runs in rounds of one workgroup per CU;
-    // pick the smaller rounds * (BM + BN), 128x64 on a tie.
-    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    auto cost = [&](int bm, int bn) {
-      constexpr int kCUs = 256;
-      return ((tiles(bm, bn) + kCUs - 1) / kCUs) * (bm + bn);
-    };
-    // K-slab counts of the GPT-2-small widths (768 and 4 * 768) are
-    // compile-time constants, so the K loop is fully unrolled: at every trip
-    // of a rolled loop the compiler waits for all loads in flight.
-    const bool big = M > 64 && cost(128, 64) <= cost(64, 64);
-    // 128x96 tiles for c_attn and c_fc when they cost less (at 1024 rows of
-    // GPT-2 small: 192 and 256 tiles, one round; measured 2-2.5 us faster
-    // per launch than 128x64)
-    constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU;
-    const bool wide = kWideEpi && M > 64 && cost(128, 96) < cost(big ? 128 : 64, 64);
-    const int g = wide ? tiles(128, 96) : big ? tiles(128, 64) : tiles(64, 64);
-    // (only the pairs a block issues: c_attn, c_fc, c_proj at K = 768, the
-    // MLP projection at K = 3072)
-    constexpr bool k768 = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_RESID;
-    constexpr bool k3072 = EPI == EPI_RESID;
-    bool done = false;
-    if constexpr (k768) {
-      if (K == 768) {
-        if constexpr (kWideEpi) {
-          if (wide) gemm_mfma_kernel<128, 96, EPI, 2, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        }
-        if (!wide) {
-          if (big) gemm_mfma_kernel<128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-          else gemm_mfma_kernel<64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        }
-        done = true;
-      }
-    }
-    if constexpr (k3072) {
-      if (K == 3072) {
-        if (big) gemm_mfma_kernel<128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        else gemm_mfma_kernel<64, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        done = true;
-      }
-    }
-    if (!done) {
-      if constexpr (kWideEpi) {
-        if (wide) gemm_mfma_kernel<128, 96, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      }
-      if (!wide) {
-        if (big) gemm_mfma_kernel<128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        else gemm_mfma_kernel<64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      }
-    }
+    dispatch_mfma<bf16_t, EPI>(static_cast<const bf16_t*>(A), lda,
+                               static_cast<const bf16_t*>(W), M, N, K, e, s);
+  } else if (dtype == NGPT_F16) {
+    dispatch_mfma<f16_t, EPI>(static_cast<const f16_t*>(A), lda,
+                              static_cast<const f16_t*>(W), M, N, K, e, s);
   } else {
     const dim3 grid((N + 15) / 16, (M + 15) / 16);
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(static_cast<const float*>(A), lda,

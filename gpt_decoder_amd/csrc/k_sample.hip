@@ -273,6 +273,8 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     float* xr = x + (size_t)b * C;
     if (dtype == NGPT_BF16)
       write_embedding((const bf16_t*)wte, (const bf16_t*)wpe, id, len, C, xr);
+    else if (dtype == NGPT_F16)
+      write_embedding((const f16_t*)wte, (const f16_t*)wpe, id, len, C, xr);
     else
       write_embedding((const float*)wte, (const float*)wpe, id, len, C, xr);
   }

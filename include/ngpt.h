@@ -36,8 +36,8 @@
  *     allocates device memory.
  *   - A handle is bound to one stream and is not thread-safe.
  *   - Element type of every weight, bias, LayerNorm parameter and KV entry is
- *     the config dtype (fp32 or bf16).  The residual stream, LayerNorm
- *     statistics, attention softmax and logits are fp32 in both modes.
+ *     the config dtype (fp32, bf16 or fp16).  The residual stream, LayerNorm
+ *     statistics, attention softmax and logits are fp32 in every mode.
  */
 #ifndef NGPT_H
 #define NGPT_H
@@ -61,15 +61,17 @@ extern "C" {
                                 or a logits row with no finite maximum)    */
 #define NGPT_E_TIMEOUT   -8  /* a wait in the one-launch decode kernel gave up */
 
-/* Element types. */
+/* Element types (the fp16 model: SDK guide "极速上手nanoGPT", section
+ * "性能优化技巧", mixed precision with float16). */
 #define NGPT_F32   0
 #define NGPT_BF16  1
+#define NGPT_F16   2
 
 /*
  * Model shape: the GPTConfig of the SDK guide ("模型架构解析"): block_size,
  * vocab_size, n_layer, n_head, n_embd, bias.  dropout is absent (inference).
  * Supported: n_embd % n_head == 0; head_dim = n_embd / n_head in {32, 64};
- * n_embd % 64 == 0 (bf16) or n_embd % 4 == 0 (fp32); n_embd <= 2048;
+ * n_embd % 64 == 0 (bf16, fp16) or n_embd % 4 == 0 (fp32); n_embd <= 2048;
  * 1 <= block_size <= 4096;
  * vocab_size >= 1; max_batch in [1, NGPT_MAX_BATCH];
  * max_prefill_tokens >= 1 bounds the sum of prompt lengths of one prefill.
@@ -85,7 +87,7 @@ typedef struct {
   int32_t block_size;
   int32_t vocab_size;
   int32_t bias;               /* 1: LayerNorm and Linear layers have biases */
-  int32_t dtype;              /* NGPT_F32 or NGPT_BF16 */
+  int32_t dtype;              /* NGPT_F32, NGPT_BF16 or NGPT_F16 */
   int32_t max_batch;
   int32_t max_prefill_tokens;
 } ngpt_config;

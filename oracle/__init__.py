@@ -37,13 +37,13 @@ The absolute logits of any *trained* GPT-2 are parity unpinned: the pages
 print no numeric example and no trained weights are available.
 """
 from .gpt import (OracleGPT, layer_norm, gelu, linear, causal_attention,
-                  softmax_rows, cross_entropy_rows, round_bf16, count_parameters,
+                  softmax_rows, cross_entropy_rows, round_bf16, round_fp16, count_parameters,
                   param_count_closed_form, param_count_page_estimate)
 from .sampler import sample_rows, sample_row, topk_keep_set
 
 __all__ = [
     "OracleGPT", "layer_norm", "gelu", "linear", "causal_attention",
-    "softmax_rows", "cross_entropy_rows", "round_bf16", "count_parameters",
+    "softmax_rows", "cross_entropy_rows", "round_bf16", "round_fp16", "count_parameters",
     "param_count_closed_form", "param_count_page_estimate",
     "sample_rows", "sample_row", "topk_keep_set",
 ]

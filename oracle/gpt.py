@@ -5,7 +5,9 @@ the pages; see the package docstring for the page list.
 
 Precision modes.  ``act_bf16=False`` evaluates the model exactly as defined
 (in the compute dtype) on the given weights.  ``act_bf16=True`` additionally
-rounds to bfloat16 the tensors that a bf16 data path stores as bf16: the
+rounds to bfloat16 (``act_fp16=True``: to IEEE float16, the fp16 model of
+the SDK guide's mixed-precision section) the tensors that a 16-bit data path
+stores in 16 bits: the
 LayerNorm outputs that feed a matrix product, q/k/v (the KV cache and the q
 scratch), the attention output that feeds c_proj, the GELU output that feeds
 the MLP projection, and the final LayerNorm output that feeds lm_head.  The
@@ -41,6 +43,13 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16) << np.uint64(16)
     return (u.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest IEEE binary16 value (ties to even), returned as
+    float64, after first rounding to float32 (as a float32 producer holds
+    it).  numpy's float32 -> float16 conversion is that rounding."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
 
 
 def layer_norm(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
@@ -203,14 +212,16 @@ class OracleGPT:
     """
 
     def __init__(self, cfg, weights: dict, *, act_bf16: bool = False,
-                 compute_dtype=np.float64):
+                 act_fp16: bool = False, compute_dtype=np.float64):
         self.L = cfg.n_layer
         self.H = cfg.n_head
         self.C = cfg.n_embd
         self.Tb = cfg.block_size
         self.V = cfg.vocab_size
         assert self.C % self.H == 0
+        assert not (act_bf16 and act_fp16)
         self.act_bf16 = act_bf16
+        self.act_fp16 = act_fp16
         self.dt = compute_dtype
 
         def cv(a):
@@ -229,6 +240,8 @@ class OracleGPT:
     def _act(self, a: np.ndarray) -> np.ndarray:
         if self.act_bf16:
             return round_bf16(a).astype(self.dt)
+        if self.act_fp16:
+            return round_fp16(a).astype(self.dt)
         return a
 
     # -- one block of new rows for one sequence ----------------------------
@@ -344,7 +357,7 @@ class OracleGPT:
         per-position losses [T - 1])."""
         ids = list(ids)
         lg = self.full_logits(ids, positions=list(range(len(ids))))
-        return lg, cross_entropy_rows(lg[:-1], np.asarray(ids[1:]))
+        return lg, cross_entropy_rows(lg[:-1], np.asarray(ids[1:], dtype=np.int64))
 
     def window_logits(self, tokens: Sequence[int]) -> np.ndarray:
         """generate()'s crop (serving page, section 2): the logits [V] of

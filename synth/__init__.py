@@ -60,7 +60,7 @@ class Workload:
     vocab_size: int            # padded vocabulary (logit width)
     vocab_real: int            # ids drawn from [0, vocab_real)
     bias: bool
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # "f32", "bf16" or "f16"
     batch: int
     prompt_len: int            # fixed prompt length (0 => ragged, see lens)
     prompt_len_lo: int = 0     # ragged prompt lengths uniform in [lo, hi]
@@ -142,12 +142,25 @@ def _to_bf16_values(a32: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
+def _to_f16_values(a32: np.ndarray) -> np.ndarray:
+    """float32 -> float16 (round to nearest even) -> float32, via torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a32))
+    return t.to(torch.float16).to(torch.float32).numpy()
+
+
+def _to_storage(a32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return _to_bf16_values(a32)
+    if dtype == "f16":
+        return _to_f16_values(a32)
+    return a32
+
+
 def _draw(seed: int, index: int, shape, std: float, dtype: str) -> np.ndarray:
     rng = np.random.default_rng([seed, index])
     a = (rng.standard_normal(shape) * std).astype(np.float32)
-    if dtype == "bf16":
-        a = _to_bf16_values(a)
-    return a
+    return _to_storage(a, dtype)
 
 
 def make_weights(w: Workload, *, seed: Optional[int] = None,
@@ -158,6 +171,7 @@ def make_weights(w: Workload, *, seed: Optional[int] = None,
     Layout is nanoGPT's ``nn.Linear`` layout, [out_features, in_features]
     row-major; ``attn_w`` is [3C, C] with the q rows first, then k, then v.
     For bf16 workloads every value is exactly representable in bfloat16.
+    For f16 workloads every value is exactly representable in IEEE float16.
     ``gamma_std > 0`` draws LayerNorm weights 1 + N(0, gamma_std) instead of
     ones (a test-only variant that exercises the scale path).  Biases are
     ``None`` when the workload has no biases.
@@ -173,7 +187,7 @@ def make_weights(w: Workload, *, seed: Optional[int] = None,
     def ln_w(name):
         if gamma_std > 0:
             g = 1.0 + _draw(seed, idx[name], (C,), gamma_std, "f32")
-            return _to_bf16_values(g) if dt == "bf16" else g
+            return _to_storage(g, dt)
         return np.ones((C,), np.float32)
 
     def maybe_bias(name, n):

@@ -17,6 +17,10 @@ import synth
 
 TOL_F32 = 1e-4     # max-abs logit error, fp32 data path
 TOL_BF16 = 2e-2    # max-abs logit error, bf16 data path
+# fp16 data path: the bf16 bar scaled by the ratio of the two formats' unit
+# roundoffs, 2^-11 / 2^-8 (the errors come from rounding activations to the
+# 16-bit format, and fp16 keeps three more significand bits)
+TOL_F16 = TOL_BF16 * 2.0 ** -3
 
 
 def log(*a):
@@ -31,13 +35,14 @@ def need_gpu():
 
 
 def tol_for(w) -> float:
-    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+    return {"f32": TOL_F32, "f16": TOL_F16}.get(w.dtype, TOL_BF16)
 
 
 def make_oracle(w, weights):
     """The oracle in the precision mode of the workload's data path (bf16
     rounding at the bf16 storage points for bf16 workloads)."""
-    return oracle.OracleGPT(w, weights, act_bf16=(w.dtype == "bf16"))
+    return oracle.OracleGPT(w, weights, act_bf16=(w.dtype == "bf16"),
+                            act_fp16=(w.dtype == "f16"))
 
 
 def make_exact_oracle(w, weights):

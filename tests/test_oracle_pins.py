@@ -40,6 +40,16 @@ def test_round_bf16_matches_torch_conversion():
     np.testing.assert_array_equal(oracle.round_bf16(x), want)
 
 
+def test_round_fp16_matches_torch_conversion():
+    x = np.concatenate([rng.standard_normal(20000) * 3, rng.standard_normal(2000) * 1e-5,
+                        np.array([0.0, -0.0, 1.0, 65504.0, 2.0 ** -24])])
+    want = torch.from_numpy(x).to(torch.float32).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_fp16(x), want)
+    # ties to even: 1 + 2^-11 lies halfway between 1 and 1 + 2^-10
+    assert oracle.round_fp16(np.array([1 + 2.0 ** -11]))[0] == 1.0
+    assert oracle.round_fp16(np.array([1 + 3 * 2.0 ** -11]))[0] == 1 + 2 * 2.0 ** -10
+
+
 def test_round_bf16_ties_to_even_examples():
     # 1 + 2^-8 lies halfway between bf16 1.0 and 1 + 2^-7: even is 1.0
     assert oracle.round_bf16(np.array([1.0 + 2**-8]))[0] == 1.0
@@ -215,13 +225,19 @@ def test_attention_mask_matches_page_diagram():
 BF16_POINTS = ("h1", "q", "k", "v", "y", "h2", "f", "z")
 
 
+def torch_fp16(a):
+    """Round a float64 tensor through torch's float32 and float16
+    conversions, back to float64."""
+    return a.to(torch.float32).to(torch.float16).to(torch.float64)
+
+
 def torch_bf16(a):
     """Round a float64 tensor through torch's own float32 and bfloat16
     conversions (round to nearest even), back to float64."""
     return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
-def torch_reference_logits(cfg, w, ids, cast_points=()):
+def torch_reference_logits(cfg, w, ids, cast_points=(), cast=None):
     """All-position logits of one sequence, written with torch.nn.functional
     from the page fragments: embedding sum, pre-LN blocks with SDPA
     (is_causal=True), exact GELU, tied bias-free head.
@@ -235,7 +251,8 @@ def torch_reference_logits(cfg, w, ids, cast_points=()):
     """
     t = lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float64))
     cp = set(cast_points)
-    r = lambda name, a: torch_bf16(a) if name in cp else a
+    cast = cast or torch_bf16
+    r = lambda name, a: cast(a) if name in cp else a
     C, H = cfg.n_embd, cfg.n_head
     ids_t = torch.as_tensor(np.asarray(ids), dtype=torch.long)
     T = len(ids)
@@ -467,6 +484,20 @@ def test_bf16_mode_matches_torch_model_with_bf16_casts(bias, gamma):
     mine = OracleGPT(cfg, w, act_bf16=True).full_logits(ids, positions=list(range(24)))
     want = torch_reference_logits(cfg, w, ids, cast_points=BF16_POINTS)
     np.testing.assert_allclose(mine, want, rtol=0, atol=1e-9)
+
+
+def test_fp16_mode_matches_torch_model_with_fp16_casts():
+    """The fp16 mode equals the independent torch model rounding the same
+    tensors through torch.float16 (fp16 weights, 3 blocks with biases)."""
+    cfg = small_cfg(L=3, bias=True, dtype="f16")
+    w = synth.make_weights(cfg, gamma_std=0.1)
+    ids = rng.integers(0, cfg.vocab_size, 24)
+    mine = OracleGPT(cfg, w, act_fp16=True).full_logits(ids, positions=list(range(24)))
+    want = torch_reference_logits(cfg, w, ids, cast_points=BF16_POINTS, cast=torch_fp16)
+    np.testing.assert_allclose(mine, want, rtol=0, atol=1e-9)
+    # and it is not the bf16 mode
+    other = OracleGPT(cfg, w, act_bf16=True).full_logits(ids, positions=list(range(24)))
+    assert np.max(np.abs(other - mine)) > 1e-4
 
 
 @pytest.mark.parametrize("dropped", BF16_POINTS + ("+x",))
