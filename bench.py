@@ -86,8 +86,103 @@ def prefill_flops(w, T: int) -> int:
     """Algorithmic FLOPs of a T-token prefill at batch 1: the four linear
     layers on T rows, causal attention (lower triangle only) and lm_head on
     the last row."""
+    return prefill_flops_rows(w, [T])
+
+
+def prefill_flops_rows(w, lens) -> int:
+    """Prefill FLOPs of prompts of the given lengths: linear layers on every
+    row, causal attention of each prompt (2 C T(T+1) per layer: q k^T and
+    p v over the lower triangle), lm_head on each prompt's last row."""
     C, L, V = w.n_embd, w.n_layer, w.vocab_size
-    return 2 * T * 12 * L * C * C + L * 2 * C * T * (T + 1) + 2 * C * V
+    M = int(sum(lens))
+    attn = sum(L * 2 * C * int(T) * (int(T) + 1) for T in lens)
+    return 2 * M * 12 * L * C * C + attn + len(lens) * 2 * C * V
+
+
+def eval_flops(w, T: int) -> int:
+    """FLOPs of the evaluation forward over T positions: the prefill's
+    linear layers and attention, and lm_head on every row."""
+    C, L, V = w.n_embd, w.n_layer, w.vocab_size
+    return 2 * T * 12 * L * C * C + L * 2 * C * T * (T + 1) + T * 2 * C * V
+
+
+def step_weight_bytes(w) -> int:
+    """Bytes of parameters one decode step reads once (16-bit): the four
+    matrices of every block and the tied embedding, LayerNorm weights, and
+    the biases of a model with biases."""
+    C, L, V = w.n_embd, w.n_layer, w.vocab_size
+    n = 12 * L * C * C + V * C + (2 * L + 1) * C
+    if w.bias:
+        n += L * 11 * C + C
+    return 2 * n
+
+
+def step_kv_bytes(w, positions) -> int:
+    """K and V bytes one decode step reads: for each active row with its new
+    token at position p, rows 0..p of every layer (16-bit)."""
+    return sum(2 * w.n_layer * w.n_embd * 2 * (int(p) + 1) for p in positions)
+
+
+def cpu_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def cpu_table(budget_s: float = 60.0):
+    """The oracle timed on the host at 1 thread and at all BLAS threads on
+    bounded samples of each workload: prefill tokens/s and decode tokens/s.
+    Samples (per workload, at each thread count): the tiny character model
+    in full (16-id prompt, 47 steps); the Shakespeare-char shape with its 8
+    prompts and 8 decode steps; GPT-2 124M: the 128-id prompt and 16 steps,
+    and the 1024-id prompt (prefill only); the batch-64 ragged workload on 2
+    of its sequences (prefill + 4 steps); GPT-2 XL on 1 sequence of 128 ids
+    (prefill + 2 steps, all threads only).  Rates of subsets are per token,
+    extrapolated to the workload."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits, threadpool_info
+    all_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    specs = [("char_4l128_fp32", 1, None, 47), ("char_6l384_bf16_b8", 8, None, 8),
+             ("gpt2_124m_b1", 1, None, 16), ("gpt2_124m_prefill1024", 1, None, 0),
+             ("gpt2_124m_bias_b64_ragged", 2, None, 4), ("gpt2_xl_b32", 1, 128, 2)]
+    out = {}
+    t_start = time.perf_counter()
+    for name, nseq, plen, steps in specs:
+        w = synth.workload(name)
+        if w.n_layer > 12 and time.perf_counter() - t_start > budget_s:
+            continue
+        W = synth.make_weights(w)
+        ids, lens = synth.make_prompts(w)
+        ids, lens = ids[:nseq], lens[:nseq].copy()
+        if plen:
+            lens[:] = plen
+            ids = ids[:, :plen]
+        res = {}
+        for threads in ((1, all_threads) if w.n_layer <= 12 else (all_threads,)):
+            with threadpool_limits(threads):
+                o = oracle.OracleGPT(w, W, act_bf16=(w.dtype == "bf16"))
+                t0 = time.perf_counter()
+                lg = o.prefill(ids, lens)
+                tp = time.perf_counter() - t0
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    lg = o.decode([int(np.argmax(r)) for r in lg])
+                td = time.perf_counter() - t0
+            res[f"threads_{threads}"] = {
+                "prefill_tokens_per_s": round(float(np.sum(lens)) / tp, 2),
+                "decode_tokens_per_s": round(nseq * steps / td, 2) if steps else None}
+        res["sample"] = f"{nseq} sequence(s), prompt {int(lens[0])}{'+' if len(set(lens)) > 1 else ''} ids, {steps} decode steps"
+        out[name] = res
+    model, nproc = cpu_info()
+    return {"cpu_model": model, "nproc": nproc, "blas_threads": all_threads,
+            "kind": "oracle", "workloads": out}
 
 
 def cpu_baseline(w, W, ids, lens, steps: int):
@@ -109,6 +204,99 @@ def cpu_baseline(w, W, ids, lens, steps: int):
     return steps / dt, cores
 
 
+def run_batched_workloads(torch, ng, synth):
+    """The other workloads on the GPU, one generation each after a warm-up:
+    the batch-64 ragged workload with biases (prefill of all prompts, then
+    top-k 50 sampled decode until every row holds 1024 tokens), the GPT-2 XL
+    shape at batch 32 (512-id prompts, 512 greedy steps), the
+    Shakespeare-char shape at batch 8 (64-id prompts, 192 sampled steps),
+    and the evaluation forward with labels over one 1024-id sequence.
+    Decode is reported against HBM (bytes the steps must read) and, for the
+    large batches, MFMA (their matrix-product FLOPs); prefill against MFMA."""
+    res = {}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    for name in ("gpt2_124m_bias_b64_ragged", "gpt2_xl_b32", "char_6l384_bf16_b8"):
+        w = synth.workload(name)
+        W = synth.make_weights(w)
+        ids, lens = synth.make_prompts(w)
+        steps = synth.decode_steps(w, lens)
+        uni = torch.as_tensor(synth.make_uniforms(w, steps)).cuda()
+        m = ng.model_from_workload(w, W, max_prefill_tokens=int(lens.sum()))
+        if w.greedy:
+            m.set_sampling(greedy=True)
+        else:
+            m.set_sampling(temperature=w.temperature, top_k=w.top_k)
+        kv = m.new_kv(w.batch)
+        nxt = torch.empty(w.batch, dtype=torch.int32, device="cuda")
+        d_ids = torch.as_tensor(ids).cuda()
+        t = {}
+        for rep in range(2):        # warm-up, then the timed generation
+            a, b, c = ev(), ev(), ev()
+            a.record(m.stream)
+            m.prefill(kv, d_ids, list(lens))
+            b.record(m.stream)
+            for s in range(steps):
+                m.decode_step(kv, nxt, uni[s])
+            c.record(m.stream)
+            torch.cuda.synchronize()
+            t = {"prefill_ms": a.elapsed_time(b), "decode_ms": b.elapsed_time(c)}
+        assert m.device_status() == 0
+        m.close()
+        del kv
+        C, L, V = w.n_embd, w.n_layer, w.vocab_size
+        limit = w.decode_to if w.decode_to else int(lens.max()) + steps
+        new_tokens = int(sum(min(limit, int(l) + steps) - int(l) for l in lens))
+        pos_bytes, flops = 0, 0
+        for s in range(steps):
+            act = [int(l) + s for l in lens if int(l) + s < limit]
+            pos_bytes += step_weight_bytes(w) + step_kv_bytes(w, act)
+            flops += len(act) * (2 * (12 * L * C * C + V * C)) + sum(4 * L * C * (p + 1) for p in act)
+        dec_s = t["decode_ms"] / 1e3
+        pre_flops = prefill_flops_rows(w, [int(l) for l in lens])
+        r = {"workload": w.description,
+             "prefill_tokens_per_s": round(float(lens.sum()) / (t["prefill_ms"] / 1e3), 1),
+             "prefill_ms": round(t["prefill_ms"], 3),
+             "prefill_mfma_frac": round(pre_flops / (t["prefill_ms"] / 1e3) / 1e12
+                                        / MFMA_BF16_PEAK_TFLOPS, 4),
+             "decode_tokens_per_s": round(new_tokens / dec_s, 1),
+             "decode_us_per_step": round(t["decode_ms"] * 1e3 / steps, 2),
+             "decode_steps": steps,
+             "decode_hbm_frac": round(pos_bytes / dec_s / 1e9 / HBM_PEAK_GBS, 4),
+             "decode_mfma_frac": round(flops / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        res[name] = r
+        print(json.dumps({"batched": name, **r}), file=sys.stderr, flush=True)
+
+    # evaluation forward with labels over 1024 positions
+    wp = synth.workload("gpt2_124m_prefill1024")
+    W = synth.make_weights(wp)
+    ids, lens = synth.make_prompts(wp)
+    m = ng.model_from_workload(wp, W, max_batch=1, max_prefill_tokens=1024)
+    kv = m.new_kv(1)
+    lg = torch.empty((1024, wp.vocab_size), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        m.eval_loss(kv, ids, list(lens), logits=lg)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    reps = 10
+    a.record(m.stream)
+    for _ in range(reps):
+        m.eval_loss(kv, ids, list(lens), logits=lg)
+    b.record(m.stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    m.close()
+    res["eval_1024"] = {"workload": "GPT-2 124M shape, one 1024-id sequence, logits at every "
+                                    "position and the shifted cross-entropy",
+                        "us": round(us, 2),
+                        "tokens_per_s": round(1024 / (us * 1e-6), 1),
+                        "mfma_frac": round(eval_flops(wp, 1024) / (us * 1e-6) / 1e12
+                                           / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +307,10 @@ def main():
                     help="decode steps of the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter scaling)")
+    ap.add_argument("--no-batched", dest="batched", action="store_false",
+                    help="skip the batched workloads (batch 8 / 64 / XL 32) and the eval forward")
+    ap.add_argument("--cpu-table", type=float, default=60.0,
+                    help="seconds budget of the CPU-oracle table (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
@@ -205,11 +397,14 @@ def main():
     pre_us = pa.elapsed_time(pb) * 1000.0 / args.prefill_reps
     pre_tflops = prefill_flops(wp, 1024) / (pre_us * 1e-6) / 1e12
 
+    extra = run_batched_workloads(torch, ng, synth) if args.batched else {}
+
     cpu = None
     if args.cpu_steps > 0:
         rate, cores = cpu_baseline(w, W, ids, lens, args.cpu_steps)
+        model, nproc = cpu_info()
         cpu = {"value": round(rate, 3), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
+               "kind": "oracle", "nproc": nproc, "cpu_model": model,
                "sample": f"GPT-2 124M shape, batch 1: 128-id prefill then "
                          f"{args.cpu_steps} greedy KV-cached decode steps "
                          "(numpy fp64 oracle, bf16 activation rounding)"}
@@ -247,6 +442,9 @@ def main():
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "cpu_baseline": cpu,
     }
+    out.update(extra)
+    if cpu is not None and args.cpu_table > 0:
+        out["cpu_table"] = cpu_table(args.cpu_table)
     print(json.dumps(out), flush=True)
 
 

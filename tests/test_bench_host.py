@@ -55,6 +55,27 @@ def test_prefill_flops_equal_a_loop_count():
     assert bench.prefill_flops(w, T) == flops
 
 
+def test_batched_counts_equal_loop_counts():
+    """The batched workloads' numerators: a step reads every parameter once
+    (with biases when the model has them) plus each active row's K/V rows;
+    ragged prefill FLOPs sum each prompt's lower triangle; the evaluation
+    forward adds lm_head on every row."""
+    w = synth.Workload("tiny_bias", 6, 2, 2, 64, 32, 97, 97, True, "bf16", batch=3,
+                       prompt_len=4)
+    W = synth.make_weights(w)
+    n = W["wte"].size + W["lnf_w"].size + W["lnf_b"].size
+    for lw in W["layers"]:
+        n += sum(t.size for t in lw.values() if t is not None)
+    assert bench.step_weight_bytes(w) == 2 * n
+    pos = [3, 7, 0]
+    assert bench.step_kv_bytes(w, pos) == sum(2 * 2 * w.n_layer * w.n_embd * (p + 1) for p in pos)
+    lens = [5, 9, 1]
+    assert bench.prefill_flops_rows(w, lens) == (
+        sum(bench.prefill_flops(w, T) for T in lens))
+    C, L, V, T = w.n_embd, w.n_layer, w.vocab_size, 9
+    assert bench.eval_flops(w, T) == bench.prefill_flops(w, T) + (T - 1) * 2 * C * V
+
+
 def test_traffic_summary_is_used_only_for_the_current_kernel_sources(tmp_path, monkeypatch):
     good = tmp_path / "good.txt"
     good.write_text(f"kernel_source_sha256: {bench.kernel_sources_sha256()}\n"
