@@ -135,7 +135,7 @@ std::string g_static_error;
 // name as an address: each device's address comes from hipGetSymbolAddress
 // (taken once per device, with the device current) and is what the kernels
 // receive.
-constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+constexpr size_t kStaticWorkspaceBytes = NGPT_STATIC_WORKSPACE_BYTES;
 struct StaticSlot {
   void* ptr = nullptr;   // device address of `scratch` on this device
   bool live = false;     // a model currently uses it

@@ -33,7 +33,8 @@
  *   - All device memory is caller-owned and borrowed: weights, the KV cache
  *     and the workspace (sized by ngpt_workspace_bytes()) must stay alive and
  *     unmodified by others while the model uses them.  The library never
- *     allocates device memory.
+ *     allocates device memory (ngpt_create_static() takes its workspace
+ *     from a fixed array of the library instead of the caller).
  *   - A handle is bound to one stream and is not thread-safe.
  *   - Element type of every weight, bias, LayerNorm parameter and KV entry is
  *     the config dtype (fp32, bf16 or fp16).  The residual stream, LayerNorm
@@ -179,6 +180,23 @@ int ngpt_check_config(const ngpt_config *cfg);
 int ngpt_create(const ngpt_config *cfg, const ngpt_weights *w,
                 void *workspace, size_t ws_bytes, void *stream,
                 ngpt_model **out);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): ngpt_create()
+ * with the workspace taken from a fixed array inside the library, one per
+ * GPU, of NGPT_STATIC_WORKSPACE_BYTES bytes, held until the process ends.
+ * Calls no hipMalloc, hipFree or other allocating routine; the array is
+ * zeroed on the stream at creation.  Every model created this way on a
+ * device shares that device's array, so at most one may be alive per device
+ * at a time: a second create on the same device fails with NGPT_E_ARG until
+ * the first is destroyed (calls that overlapped on one array would race).
+ * Errors: as ngpt_create, and NGPT_E_SIZE when ngpt_workspace_bytes(cfg)
+ * exceeds the array.
+ */
+#define NGPT_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int ngpt_create_static(const ngpt_config *cfg, const ngpt_weights *w,
+                       void *stream, ngpt_model **out);
 
 /* Wait for the stream, then release the handle (the caller still owns the
  * workspace, weights and KV memory).  The only call that synchronises. */
