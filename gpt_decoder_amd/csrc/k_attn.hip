@@ -29,7 +29,7 @@
 namespace ngpt {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPrefillKch = 4;   // key tiles per chunk when a prefill tile is split
+constexpr int kPrefillKch = 8;   // key tiles per chunk when a prefill tile is split
 
 // ---------------------------------------------------------------------------
 // Prefill, bf16 MFMA.  Scores are formed transposed, S^T = K Q^T, so that a

@@ -490,17 +490,17 @@ def test_prefill_key_split_head_sizes(H, C):
     chunks whose (max, sum, output) records a second kernel merges in chunk
     order; both head sizes (32 and 64) against the oracle's prefill."""
     need_gpu()
-    V = 300
-    w = synth.Workload(f"split_{H}_{C}", 19, 2, H, C, 512, V, V, False, "bf16",
-                       batch=1, prompt_len=450)
+    V, T = 300, 970    # 16 key tiles: the last query tiles take 2 chunks of 8
+    w = synth.Workload(f"split_{H}_{C}", 19, 2, H, C, 1024, V, V, False, "bf16",
+                       batch=1, prompt_len=T)
     W = synth.make_weights(w)
-    ids = np.random.default_rng(H).integers(0, V, (1, 450)).astype(np.int32)
+    ids = np.random.default_rng(H).integers(0, V, (1, T)).astype(np.int32)
     m = make_model(w, W)
     kv = m.new_kv(1)
     o = oracle.OracleGPT(w, W, act_bf16=True)
-    err = max_abs(gpu_prefill(m, kv, ids, [450]), o.prefill(ids, [450]))
+    err = max_abs(gpu_prefill(m, kv, ids, [T]), o.prefill(ids, [T]))
     assert m.device_status() == 0
-    log(f"  hs={C // H}: 450-token prefill, max logit err {err:.2e}")
+    log(f"  hs={C // H}: {T}-token prefill, max logit err {err:.2e}")
     assert err < TOL_BF16
     m.close()
 

@@ -76,25 +76,26 @@ def test_extend_chunks_against_oracle(dtype, H, C):
 
 
 def test_extend_batch1_long_past_key_split():
-    """Batch 1, bf16: a 300-token prompt, then a 200-token chunk (the key
-    split path with a past, 8 key tiles per query tile) and a 1-token chunk."""
+    """Batch 1, bf16: a 300-token prompt, then a 500-token chunk (the key
+    split path with a past: up to 13 key tiles per query tile, in chunks of
+    8) and a 1-token chunk at position 800."""
     need_gpu()
-    w = small("bf16", L=2, H=4, C=256, Tb=512, batch=1)
+    w = small("bf16", L=2, H=4, C=256, Tb=1024, batch=1)
     W = synth.make_weights(w)
     rng = np.random.default_rng(6)
-    toks = rng.integers(0, w.vocab_size, 501).astype(np.int32)
+    toks = rng.integers(0, w.vocab_size, 801).astype(np.int32)
     m = make_model(w, W, max_batch=1, max_prefill_tokens=512)
     kv = m.new_kv(1)
     o = oracle_for(w, W)
     m.prefill(kv, toks[None, :300], [300])
     errs = [max_abs(m.logits(1).cpu().numpy()[0], o.prefill(toks[None, :300], [300])[0])]
-    m.extend(kv, [0], toks[None, 300:500], [200])
-    errs.append(max_abs(m.logits(1).cpu().numpy()[0], o.extend(0, toks[300:500])))
-    m.extend(kv, [0], toks[None, 500:501], [1])
-    errs.append(max_abs(m.logits(1).cpu().numpy()[0], o.extend(0, toks[500:501])))
+    m.extend(kv, [0], toks[None, 300:800], [500])
+    errs.append(max_abs(m.logits(1).cpu().numpy()[0], o.extend(0, toks[300:800])))
+    m.extend(kv, [0], toks[None, 800:801], [1])
+    errs.append(max_abs(m.logits(1).cpu().numpy()[0], o.extend(0, toks[800:801])))
     log(f"  batch-1 extend with key split: errs {['%.1e' % e for e in errs]}")
     assert max(errs) < TOL_BF16
-    assert kv.lens.cpu().tolist() == [501]
+    assert kv.lens.cpu().tolist() == [801]
     m.close()
 
 
