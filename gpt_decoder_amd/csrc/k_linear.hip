@@ -247,6 +247,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
       if constexpr (LNA) {
+        // slabs past K (the loop's padding to a multiple of S) are zeros,
+        // as the plain path's range-checked loads give: the gain / shift
+        // staging holds only K entries
+        if (k0 >= K) {
+          *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) = make_uint4(0, 0, 0, 0);
+          continue;
+        }
         const int kc = k0 + (c & 7) * 8;
         const uint4 a0 = ra[st][i][0], a1 = ra[st][i][1];
         const float xv[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z),

@@ -5,9 +5,9 @@
 // value below the k-th largest (k = min(top_k, vocab)) by -inf, applies a
 // softmax and draws one id with torch.multinomial.  Here the draw is the
 // inverse CDF of the caller's uniform u in [0, 1):
-//   s_i = float32(logit_i / T), correctly rounded (the quotient is formed in
-//         double, whose 53-bit significand makes the final rounding to
-//         float32 exact);
+//   s_i = float32(logit_i / T), correctly rounded (IEEE fp32 division; the
+//         same value as the quotient formed in double and then rounded, since
+//         53 >= 2 * 24 + 2 makes that double rounding innocuous);
 //   kept set K = {i : s_i >= v}, v the k-th largest s (ties kept);
 //   w_i = exp(double(s_i) - max s), S = sum over K;
 //   id  = smallest i in K whose running sum (ascending ids) exceeds u * S,
@@ -16,9 +16,10 @@
 //
 // One 512-thread workgroup per row.  The k-th largest value is found by a
 // radix select over order-preserving 32-bit keys, most significant byte
-// first.  The running sum is a two-level scan: each thread owns a contiguous
-// run of ids, the per-thread totals are scanned, then the owning thread walks
-// its run.
+// first, with the histogram adds aggregated per wavefront.  The running sum
+// is a two-level scan: each thread owns a contiguous run of ids, the
+// per-thread totals are prefix-summed across the workgroup, then the owning
+// thread walks its run.
 #include <math.h>
 
 #include "common.hpp"
@@ -28,8 +29,11 @@ namespace ngpt {
 
 constexpr int kSampThreads = 512;
 
+// logit / T rounded once to fp32: the fp32 division here is IEEE
+// correctly rounded (the compiler's default division, no fast-math), so it
+// equals the quotient formed in fp64 and then rounded.
 __device__ __forceinline__ float scaled(float logit, float T) {
-  return (float)((double)logit / (double)T);
+  return logit / T;
 }
 
 // Order-preserving key: larger float <=> larger key; -0 is folded into +0.
@@ -48,7 +52,7 @@ struct SampShared {
   double dred[kSampThreads / 64];
   float fred[kSampThreads / 64];
   int ired[kSampThreads / 64];
-  double scan[kSampThreads];
+  double scan[1];
   uint32_t prefix;
   uint32_t remaining;
   int found;
@@ -121,6 +125,38 @@ __device__ int row_argmax(const float* lg, int V, SampShared& sh) {
   return r;   // 0x7FFFFFFF: no finite maximum (all -inf or NaN)
 }
 
+// Wavefront-aggregated histogram add: the lanes with `match` add 1 to
+// hist[bin]; lanes sharing a bin are counted with one atomic (logits crowd
+// into a few top-byte bins, where per-lane atomics would serialise).
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool match, uint32_t bin) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long act = __ballot(match);
+  while (act) {
+    const int leader = __ffsll(act) - 1;
+    const uint32_t lbin = __shfl(bin, leader, 64);
+    const unsigned long long same = __ballot(match && bin == lbin);
+    if (lane == leader) atomicAdd(&hist[lbin], (uint32_t)__popcll(same));
+    act &= ~same;
+  }
+}
+
+// Inclusive prefix sums of one double per thread over the workgroup, in a
+// fixed order (shuffles within each wavefront, then the wavefront totals).
+__device__ __forceinline__ double block_scan_incl(double v, SampShared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  __syncthreads();
+  if (lane == 63) sh.dred[w] = v;
+  __syncthreads();
+  double before = 0.0;
+  for (int i = 0; i < w; ++i) before += sh.dred[i];
+  return before + v;
+}
+
 __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
                           SampShared& sh) {
   const int tid = threadIdx.x;
@@ -134,9 +170,10 @@ __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
       for (int i = tid; i < 256; i += kSampThreads) sh.hist[i] = 0;
       __syncthreads();
       const uint32_t prefix = sh.prefix;
-      for (int i = tid; i < V; i += kSampThreads) {
-        const uint32_t k = fkey(scaled(lg[i], T));
-        if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 0xFFu], 1u);
+      for (int i0 = 0; i0 < V; i0 += kSampThreads) {   // uniform trip count
+        const int i = i0 + tid;
+        const uint32_t k = i < V ? fkey(scaled(lg[i], T)) : 0u;
+        hist_add(sh.hist, i < V && (k & mask) == prefix, (k >> shift) & 0xFFu);
       }
       __syncthreads();
       if (tid == 0) {
@@ -172,22 +209,16 @@ __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
       last_kept = i;
     }
   }
-  sh.scan[tid] = local;
+  const double incl = block_scan_incl(local, sh);
   __syncthreads();
+  if (tid == kSampThreads - 1) sh.scan[0] = incl;   // total S
   if (tid == 0) {
-    double acc = 0.0;
-    for (int t = 0; t < kSampThreads; ++t) {
-      const double v = sh.scan[t];
-      sh.scan[t] = acc;   // exclusive prefix
-      acc += v;
-    }
-    sh.dred[0] = acc;     // total S
     sh.found = 0x7FFFFFFF;
     sh.last_kept = -1;
   }
   __syncthreads();
-  const double target = u * sh.dred[0];
-  double c = sh.scan[tid];
+  const double target = u * sh.scan[0];
+  double c = incl - local;   // exclusive prefix
   int hit = 0x7FFFFFFF;
   if (i0 < i1 && c + local > target) {
     for (int i = i0; i < i1; ++i) {
@@ -261,8 +292,9 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
         if (threadIdx.x == 0) atomicOr(status, 1);
         id = 0;
       }
-    } else
+    } else {
       id = row_sample(lg, V, p.temperature, p.top_k, uniforms[b], sh);
+    }
   }
   if (threadIdx.x == 0) {
     if (next_ids) next_ids[b] = id;
