@@ -171,30 +171,4 @@ __device__ __forceinline__ float wave_sum_all(float v) {
   return v;
 }
 
-// (mean, sum of squared deviations) of each 32-column slice of the row
-// x[c] = te[c] + pe[c] (0 <= c < C, C a multiple of 32), written to
-// st[2 * slice]; half a wavefront per slice, all threads of the workgroup
-// take part (blockDim a multiple of 64).  The statistics a LayerNorm of the
-// row is assembled from (see the tile GEMM's LayerNorm on load).
-template <class T>
-__device__ void embed_slice_stats(const T* te, const T* pe, int C, float* st) {
-  const int lane32 = threadIdx.x & 31;
-  const int nsl = C / 32, per = blockDim.x >> 5;
-  for (int sl = threadIdx.x >> 5; sl < ((nsl + per - 1) / per) * per; sl += per) {
-    const int c = sl * 32 + lane32;
-    const float v = sl < nsl ? to_f32(te[c]) + to_f32(pe[c]) : 0.f;
-    float sum = v;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
-    const float mean = sum * (1.0f / 32);
-    float d2 = (v - mean) * (v - mean);
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) d2 += __shfl_xor(d2, o, 32);
-    if (lane32 == 0 && sl < nsl) {
-      st[2 * sl] = mean;
-      st[2 * sl + 1] = d2;
-    }
-  }
-}
-
 }  // namespace ngpt

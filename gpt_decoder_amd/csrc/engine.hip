@@ -148,7 +148,7 @@ std::map<int, StaticSlot> g_static_slots;
 // Byte offsets of the workspace regions (every region 256-byte aligned).
 struct WsLayout {
   size_t x, h, q, y, f, z, logits, row_b, row_pos, last_rows, last_slot, hist,
-      part, ppart, ids, tok, pos, status, params, done, st_a, st_b;
+      part, ppart, ids, tok, pos, status, params, done;
   // one-launch decode exchange buffers (absent: persist_shape == false)
   bool persist_shape = false;
   size_t eq, er, ey, e1, ef, e2, epoch, ecand, dlayers;
@@ -174,7 +174,6 @@ struct ngpt_model {
   int32_t *row_b = nullptr, *row_pos = nullptr, *last_rows = nullptr;
   int32_t* last_slot = nullptr;  // cache row of each prefilled sequence
   int32_t* hist = nullptr;       // token history [max_batch][Tb]
-  float *st_a = nullptr, *st_b = nullptr;  // LayerNorm slice statistics of x
   float* part = nullptr;
   float* ppart = nullptr;   // prefill attention key-split partials (one sequence)
   int32_t* d_ids = nullptr; // packed prompt ids copied from the host
@@ -293,8 +292,6 @@ static WsLayout ws_layout(const ngpt_config* cfg) {
   o.logits = carve(Bm * (size_t)cfg->vocab_size * 4);
   o.row_b = carve(Mm * 4); o.row_pos = carve(Mm * 4); o.last_rows = carve(Bm * 4);
   o.last_slot = carve(Bm * 4); o.hist = carve(Bm * (size_t)Tb * 4);
-  // LayerNorm row statistics (32-column slices) left by the residual writers
-  o.st_a = carve(Mm * (C / kStatSlice) * 2 * 4); o.st_b = carve(Mm * (C / kStatSlice) * 2 * 4);
   o.part = carve(Bm * H * (size_t)nchunk * (hs + 2) * 4);
   o.ppart = carve((size_t)H * Tb * attn_prefill_split_chunks(Tb) * (hs + 4) * 4);
   o.ids = carve((size_t)cfg->max_prefill_tokens * 4);
@@ -377,7 +374,6 @@ static int create_on(const ngpt_config* cfg, const ngpt_weights* w, void* ws,
   m->row_b = (int32_t*)(base + o.row_b); m->row_pos = (int32_t*)(base + o.row_pos);
   m->last_rows = (int32_t*)(base + o.last_rows); m->part = (float*)(base + o.part);
   m->last_slot = (int32_t*)(base + o.last_slot); m->hist = (int32_t*)(base + o.hist);
-  m->st_a = (float*)(base + o.st_a); m->st_b = (float*)(base + o.st_b);
   m->ppart = (float*)(base + o.ppart);
   m->d_ids = (int32_t*)(base + o.ids);
   m->tok = (int32_t*)(base + o.tok);
@@ -687,22 +683,14 @@ static void enqueue_blocks(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int T
   hipStream_t s = m->stream;
   m->cand_ok = false;   // the logits are about to come from this prefill
   set_lens_kernel<<<(kv->batch + 63) / 64, 64, 0, s>>>(pl.la, kv->lens, kv->limit);
-  // Prefill reads materialised LayerNorm outputs: normalising x on the
-  // tile GEMMs' loads instead (the residual writers leaving slice
-  // statistics) measured slower at 1024 rows, 992 -> 1271 us, as the fp32 A
-  // operand doubles the tile loads and the normalisation sits between load
-  // and LDS store.
-  float* sa = nullptr;
-  float* sb = nullptr;
   launch_embed_prefill(dt, ids, Tmax, map, M, m->wte, m->wpe, C, m->V, m->x,
                        m->row_b, m->row_pos, m->last_rows, m->last_slot, m->hist,
-                       m->Tb, m->status, sa, s);
+                       m->Tb, m->status, s);
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, kv->batch);
     void* vl = layer_cache(m, kv->v, l, kv->batch);
-    LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
-    ln1.stats = sa;
+    const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = m->row_b; eq.row_pos = m->row_pos;
@@ -711,15 +699,14 @@ static void enqueue_blocks(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int T
     launch_attn_prefill(dt, m->q, C, kl, vl, map, pl.maxlen, m->H, m->hs, m->Tb,
                         m->y, C, m->ppart, s);
     EpiArgs ep;
-    ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C; ep.stats = sb;
+    ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
     launch_linear(dt, EPI_RESID, m->y, C, nullptr, w.attnproj_w, M, C, C, ep, s);
-    LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
-    ln2.stats = sb;
+    const LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
     EpiArgs ef;
     ef.bias = w.fc_b; ef.out = m->f; ef.ldo = 4 * C;
     launch_linear(dt, EPI_GELU, nullptr, C, &ln2, w.fc_w, M, 4 * C, C, ef, s);
     EpiArgs em;
-    em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C; em.stats = sa;
+    em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
     launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, M, C, 4 * C, em, s);
   }
 }
@@ -818,11 +805,11 @@ int ngpt_eval_loss(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, const int32_t
   hipStream_t s = m->stream;
   m->cand_ok = false;
   enqueue_blocks(m, kv, m->d_ids, 0, pl);
-  // ln_f and the tied lm_head on every row (through the h rows)
-  LnArgs lnf{m->x, C, m->lnf_w, m->lnf_b, m->h};
+  // ln_f and the tied lm_head on every row (the h rows hold M x C)
+  launch_layernorm(dt, m->x, C, nullptr, M, m->lnf_w, m->lnf_b, m->h, C, C, s);
   EpiArgs el;
   el.out = logits; el.ldo = m->V;
-  launch_linear(dt, EPI_LOGITS, nullptr, C, &lnf, m->wte, M, m->V, C, el, s);
+  launch_linear(dt, EPI_LOGITS, m->h, C, nullptr, m->wte, M, m->V, C, el, s);
   launch_cross_entropy(logits, m->V, m->V, M, M - B, m->d_ids, m->row_b, m->last_rows,
                        losses, mean_loss, s);
   hipError_t e = hipGetLastError();
@@ -922,28 +909,17 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   return a;
 }
 
-// Whether the per-layer decode forward runs on the 16-bit tile path, where
-// the residual writers leave LayerNorm slice statistics (st_a: the head
-// node's embedding and each MLP projection; st_b: each attention c_proj)
-// and the GEMMs after them apply the LayerNorm on load.
-static bool decode_stats(const ngpt_model* m, int Bk) {
-  return m->cfg.dtype != NGPT_F32 && !decode_fused_proj(Bk);
-}
-
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
   if (m->persist && Bk == 1) {
     launch_decode_persistent(persist_args(m, kv), m->persist_grid, s);
     return;
   }
-  float* sa = decode_stats(m, Bk) ? m->st_a : nullptr;
-  float* sb = decode_stats(m, Bk) ? m->st_b : nullptr;
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
     void* kl = layer_cache(m, kv->k, l, Bk);
     void* vl = layer_cache(m, kv->v, l, Bk);
-    LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
-    ln1.stats = sa;
+    const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = nullptr; eq.row_pos = m->pos;
@@ -953,23 +929,21 @@ static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t
     launch_attn_decode(dt, m->q, kl, vl, m->pos, Bk, m->H, m->hs, m->Tb,
                        m->part, m->y, !fused, s);
     EpiArgs ep;
-    ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C; ep.stats = sb;
+    ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
     if (fused)
       launch_attn_proj(dt, m->part, m->pos, m->H, m->hs, m->nchunk,
                        attn_decode_chunk_keys(), w.attnproj_w, Bk, C, ep, s);
     else
       launch_linear(dt, EPI_RESID, m->y, C, nullptr, w.attnproj_w, Bk, C, C, ep, s);
-    LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
-    ln2.stats = sb;
+    const LnArgs ln2{m->x, C, w.ln2_w, w.ln2_b, m->h};
     EpiArgs ef;
     ef.bias = w.fc_b; ef.out = m->f; ef.ldo = 4 * C;
     launch_linear(dt, EPI_GELU, nullptr, C, &ln2, w.fc_w, Bk, 4 * C, C, ef, s);
     EpiArgs em;
-    em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C; em.stats = sa;
+    em.bias = w.mlpproj_b; em.out = m->x; em.ldo = C;
     launch_linear(dt, EPI_RESID, m->f, 4 * C, nullptr, w.mlpproj_w, Bk, C, 4 * C, em, s);
   }
-  LnArgs lnf{m->x, C, m->lnf_w, m->lnf_b, m->z};
-  lnf.stats = sa;
+  const LnArgs lnf{m->x, C, m->lnf_w, m->lnf_b, m->z};
   EpiArgs el;
   el.out = m->logits; el.ldo = m->V; el.row_pos = m->pos;
   launch_linear(dt, EPI_LOGITS, nullptr, C, &lnf, m->wte, Bk, m->V, C, el, s);
@@ -998,7 +972,6 @@ static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
   a.C = m->C;
   a.dtype = m->cfg.dtype;
   a.x = m->x;
-  a.stats = decode_stats(m, kv->batch) ? m->st_a : nullptr;
   return a;
 }
 

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void embed_prefill_kernel(
     float* __restrict__ x, int32_t* __restrict__ row_b,
     int32_t* __restrict__ row_pos, int32_t* __restrict__ last_rows,
     int32_t* __restrict__ last_slot, int32_t* __restrict__ hist, int Tb,
-    int32_t* __restrict__ status, float* __restrict__ stats) {
+    int32_t* __restrict__ status) {
   const int r = blockIdx.x;
   // sequence owning packed row r: the last b with off[b] <= r
   int lo = 0, hi = map.B - 1;
@@ -49,9 +49,6 @@ __global__ __launch_bounds__(256) void embed_prefill_kernel(
   float* xr = x + (size_t)r * C;
   for (int c = threadIdx.x; c < C; c += blockDim.x)
     xr[c] = to_f32(te[c]) + to_f32(pe[c]);
-  // (mean, M2) of each 32-column slice of the row, for the first block's
-  // LayerNorm on load
-  if (stats) embed_slice_stats(te, pe, C, stats + (size_t)r * (C / kStatSlice) * 2);
 }
 
 template <class T>
@@ -167,20 +164,20 @@ void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
                           const void* wpe, int C, int V, float* x,
                           int32_t* row_b, int32_t* row_pos, int32_t* last_rows,
                           int32_t* last_slot, int32_t* hist, int Tb,
-                          int32_t* status, float* stats, hipStream_t s) {
+                          int32_t* status, hipStream_t s) {
   if (M <= 0) return;
   if (dtype == NGPT_BF16)
     embed_prefill_kernel<bf16_t><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const bf16_t*)wte, (const bf16_t*)wpe, C, V, x,
-        row_b, row_pos, last_rows, last_slot, hist, Tb, status, stats);
+        row_b, row_pos, last_rows, last_slot, hist, Tb, status);
   else if (dtype == NGPT_F16)
     embed_prefill_kernel<f16_t><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const f16_t*)wte, (const f16_t*)wpe, C, V, x,
-        row_b, row_pos, last_rows, last_slot, hist, Tb, status, stats);
+        row_b, row_pos, last_rows, last_slot, hist, Tb, status);
   else
     embed_prefill_kernel<float><<<M, 256, 0, s>>>(
         ids, Tmax, map, (const float*)wte, (const float*)wpe, C, V, x, row_b,
-        row_pos, last_rows, last_slot, hist, Tb, status, stats);
+        row_pos, last_rows, last_slot, hist, Tb, status);
 }
 
 void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,

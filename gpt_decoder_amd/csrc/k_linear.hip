@@ -116,27 +116,10 @@ __device__ __forceinline__ uint2 pack4(float4 v) {
 // read-modify-write of the residual).  Both operands are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
-// Combine two (count, mean, M2) summaries of a row (Chan et al.'s parallel
-// update of the mean and the sum of squared deviations).
-__device__ __forceinline__ void stat_merge(float& n, float& mean, float& m2, float nb,
-                                           float meanb, float m2b) {
-  if (nb == 0.f) return;
-  if (n == 0.f) { n = nb; mean = meanb; m2 = m2b; return; }
-  const float nn = n + nb, d = meanb - mean;
-  mean += d * (nb / nn);
-  m2 += m2b + d * d * (n * nb / nn);
-  n = nn;
-}
-
-// With LNA the A operand is LayerNorm(x) of fp32 rows x (ln.x, ln.ldx),
-// normalised as the tile is loaded: the row statistics come from the
-// producer's 32-column slices (ln.stats), the gain and shift (ln.w, ln.b)
-// sit in LDS, and the normalised values are rounded to T as a materialised
-// LayerNorm output would be.
-template <class T, int BM, int BN, int EPI, int S, int NKC = 0, bool LNA = false>
+template <class T, int BM, int BN, int EPI, int S, int NKC = 0>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const T* __restrict__ A, int lda, const T* __restrict__ W, int M,
-    int N, int K, EpiArgs e, LnArgs ln) {
+    int N, int K, EpiArgs e) {
   typedef typename Half16<T>::vec8 vec8;
   constexpr int BK = 64;
   constexpr int LDS = BK + 8;  // padded row stride (elements)
@@ -177,26 +160,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   };
-  uint4 ra[S][ACH][LNA ? 2 : 1], rb[S][BCH];
-  const __amdgpu_buffer_rsrc_t rx_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(ln.x), (short)0,
-      LNA ? (int)((uint32_t)M * (uint32_t)ln.ldx * 4u) : 0, 0x00020000);
+  uint4 ra[S][ACH], rb[S][BCH];
   auto gload = [&](int st, int k0) {
     const bool kin = k0 < K;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
       const int row = m0 + (c >> 3), kc = (c & 7) * 8;
-      if constexpr (LNA) {
-        const uint32_t off = (kin && row < M)
-            ? ((uint32_t)row * (uint32_t)ln.ldx + (uint32_t)(k0 + kc)) * 4u : kOut;
-        ra[st][i][0] = ld16(rx_rs, off);
-        ra[st][i][1] = ld16(rx_rs, off == kOut ? kOut : off + 16u);
-      } else {
-        ra[st][i][0] = ld16(ra_rs, (kin && row < M)
-                                       ? ((uint32_t)row * (uint32_t)lda + (uint32_t)(k0 + kc)) * 2u
-                                       : kOut);
-      }
+      ra[st][i] = ld16(ra_rs, (kin && row < M)
+                                  ? ((uint32_t)row * (uint32_t)lda + (uint32_t)(k0 + kc)) * 2u
+                                  : kOut);
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
@@ -207,68 +180,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
                                   : kOut);
     }
   };
-  // LayerNorm on load: each thread's rows' mean and 1/std, from the
-  // producer's slice statistics (the 8 threads of a row each combine every
-  // 8th slice, then a fixed butterfly over them), and gain / shift in LDS
-  __shared__ float sgb[LNA ? 2 * kGemvLnMaxK : 1];
-  float mrow[LNA ? ACH : 1], rrow[LNA ? ACH : 1];
-  if constexpr (LNA) {
-    for (int k = tid; k < K; k += 256) {
-      sgb[k] = to_f32(static_cast<const T*>(ln.w)[k]);
-      sgb[kGemvLnMaxK + k] = ln.b ? to_f32(static_cast<const T*>(ln.b)[k]) : 0.f;
-    }
-    const int nstat = K / kStatSlice;
+  auto sstore = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int c = tid + i * 256;
-      const int row = min(m0 + (c >> 3), M - 1);
-      float n = 0.f, mean = 0.f, m2 = 0.f;
-      for (int t = c & 7; t < nstat; t += 8) {
-        const float2 st = *reinterpret_cast<const float2*>(ln.stats + ((size_t)row * nstat + t) * 2);
-        stat_merge(n, mean, m2, (float)kStatSlice, st.x, st.y);
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const float nb = __shfl_xor(n, o, 64), mb = __shfl_xor(mean, o, 64),
-                    qb = __shfl_xor(m2, o, 64);
-        // the lower lane of each pair is the first operand, so both lanes
-        // compute the same combination
-        if (lane & o) { float n2 = nb, me2 = mb, q2 = qb; stat_merge(n2, me2, q2, n, mean, m2);
-                        n = n2; mean = me2; m2 = q2; }
-        else stat_merge(n, mean, m2, nb, mb, qb);
-      }
-      mrow[i] = mean;
-      rrow[i] = 1.0f / sqrtf(m2 / (float)K + 1e-5f);
-    }
-    __syncthreads();   // sgb before the first tile store reads it
-  }
-  auto sstore = [&](int st, int buf, int k0) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + i * 256;
-      if constexpr (LNA) {
-        // slabs past K (the loop's padding to a multiple of S) are zeros,
-        // as the plain path's range-checked loads give: the gain / shift
-        // staging holds only K entries
-        if (k0 >= K) {
-          *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) = make_uint4(0, 0, 0, 0);
-          continue;
-        }
-        const int kc = k0 + (c & 7) * 8;
-        const uint4 a0 = ra[st][i][0], a1 = ra[st][i][1];
-        const float xv[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z),
-                             __uint_as_float(a0.w), __uint_as_float(a1.x), __uint_as_float(a1.y),
-                             __uint_as_float(a1.z), __uint_as_float(a1.w)};
-        float hv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          hv[q] = (xv[q] - mrow[i]) * rrow[i] * sgb[kc + q] + sgb[kGemvLnMaxK + kc + q];
-        *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) =
-            make_uint4(Half16<T>::pack2(hv[0], hv[1]), Half16<T>::pack2(hv[2], hv[3]),
-                       Half16<T>::pack2(hv[4], hv[5]), Half16<T>::pack2(hv[6], hv[7]));
-      } else {
-        *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) = ra[st][i][0];
-      }
+      *reinterpret_cast<uint4*>(sA[buf] + (c >> 3) * LDS + (c & 7) * 8) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
@@ -324,7 +240,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     for (int st = 0; st < S; ++st) {
       const int it = it0 + st;
       const int buf = st & 1;   // S is even, so it % 2 == st % 2
-      sstore(st, buf, it * BK);
+      sstore(st, buf);
       __syncthreads();
       gload(st, (it + S) * BK);
 #pragma unroll
@@ -396,43 +312,6 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
           if (col + 2 < N) o[2] = from_f32<T>(v.z);
           if (col + 3 < N) o[3] = from_f32<T>(v.w);
         }
-      }
-  } else if (EPI == EPI_RESID && e.stats) {
-    // the new residual rows, and each row's (mean, M2) over this
-    // wavefront's 32 columns (WN == 32: lanes l % 16 of the two column
-    // fragments), two passes over the stored values
-    static_assert(EPI != EPI_RESID || WN == kStatSlice, "stat slices are one wavefront wide");
-    const int nstat = N / kStatSlice;
-    const int slice = (n0 + wn * WN) / kStatSlice;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
-        float val[TN];
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WN + j * 16 + (lane & 15);
-          float* o = static_cast<float*>(e.out) + (size_t)min(row, M - 1) * e.ldo + col;
-          float a = acc[i][j][v];
-          if (e.bias) a += to_f32(static_cast<const T*>(e.bias)[col]);
-          if constexpr (kPreRes) val[j] = res[i][j][v] + a;
-          else val[j] = *o + a;
-          if (row < M) *o = val[j];
-          sum += val[j];
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-        const float mean = sum * (1.0f / kStatSlice);
-        float d2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) d2 += (val[j] - mean) * (val[j] - mean);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) d2 += __shfl_xor(d2, o, 64);
-        if ((lane & 15) == 0 && row < M)
-          *reinterpret_cast<float2*>(e.stats + ((size_t)row * nstat + slice) * 2) =
-              make_float2(mean, d2);
       }
   } else {
 #pragma unroll
@@ -868,10 +747,9 @@ static void gemv_rows(const T* A, int lda, const LnArgs& ln, const T* W, int M,
 
 
 // 16-bit MFMA tile GEMM: tile shape and K-slab staging chosen per shape.
-// With LNA the A operand is LayerNorm(ln.x), normalised on load.
-template <class T, int EPI, bool LNA = false>
+template <class T, int EPI>
 static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
-                          const EpiArgs& e, const LnArgs& ln, hipStream_t s) {
+                          const EpiArgs& e, hipStream_t s) {
   // Tile size: a workgroup's time is set by the operand bytes it streams,
   // (BM + BN) * K, and the grid runs in rounds of one workgroup per CU;
   // pick the smaller rounds * (BM + BN), 128x64 on a tie.
@@ -893,34 +771,34 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   // (only the pairs a block issues: c_attn, c_fc, c_proj at K = 768, the
   // MLP projection at K = 3072)
   constexpr bool k768 = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_RESID;
-  constexpr bool k3072 = EPI == EPI_RESID && !LNA;
+  constexpr bool k3072 = EPI == EPI_RESID;
   bool done = false;
   if constexpr (k768) {
     if (K == 768) {
       if constexpr (kWideEpi) {
-        if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 2, 12, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
+        if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 2, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
       }
       if (!wide) {
-        if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 12, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
-        else gemm_mfma_kernel<T, 64, 64, EPI, 4, 12, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
+        if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<T, 64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
       }
       done = true;
     }
   }
   if constexpr (k3072) {
     if (K == 3072) {
-      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
-      else gemm_mfma_kernel<T, 64, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
+      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 4, 48><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
       done = true;
     }
   }
   if (!done) {
     if constexpr (kWideEpi) {
-      if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 4, 0, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
+      if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
     }
     if (!wide) {
-      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 0, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
-      else gemm_mfma_kernel<T, 64, 64, EPI, 8, 0, LNA><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e, ln);
+      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
     }
   }
 }
@@ -949,42 +827,17 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
     else dispatch_gemv<float, EPI>(A, lda, ln, W, M, N, K, e, s);
     return;
   }
-  // the residual epilogue's row statistics are written only on the 16-bit
-  // tile path with whole 64-column tiles
-  EpiArgs ee = e;
-  if (!half || N % 64 != 0) ee.stats = nullptr;
-  // 16-bit tiles take the LayerNorm on load when the producer left the row
-  // statistics (K within the gain / shift staging); otherwise they read a
-  // materialised LayerNorm output
-  constexpr bool kLnEpi = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_LOGITS;
-  const bool ln_on_load = kLnEpi && half && ln && ln->stats && K <= kGemvLnMaxK &&
-                          K % kStatSlice == 0;
-  if (ln && !ln_on_load) {
+  if (ln) {  // tiled paths read a materialised LayerNorm output
     launch_layernorm(dtype, ln->x, ln->ldx, nullptr, M, ln->w, ln->b, ln->h, K, K, s);
     A = ln->h;
     lda = K;
   }
-  const LnArgs none{};
   if (dtype == NGPT_BF16) {
-    if constexpr (kLnEpi) {
-      if (ln_on_load) {
-        dispatch_mfma<bf16_t, EPI, true>(nullptr, 0, static_cast<const bf16_t*>(W), M, N, K,
-                                         ee, *ln, s);
-        return;
-      }
-    }
     dispatch_mfma<bf16_t, EPI>(static_cast<const bf16_t*>(A), lda,
-                               static_cast<const bf16_t*>(W), M, N, K, ee, none, s);
+                               static_cast<const bf16_t*>(W), M, N, K, e, s);
   } else if (dtype == NGPT_F16) {
-    if constexpr (kLnEpi) {
-      if (ln_on_load) {
-        dispatch_mfma<f16_t, EPI, true>(nullptr, 0, static_cast<const f16_t*>(W), M, N, K,
-                                        ee, *ln, s);
-        return;
-      }
-    }
     dispatch_mfma<f16_t, EPI>(static_cast<const f16_t*>(A), lda,
-                              static_cast<const f16_t*>(W), M, N, K, ee, none, s);
+                              static_cast<const f16_t*>(W), M, N, K, e, s);
   } else {
     const dim3 grid((N + 15) / 16, (M + 15) / 16);
     gemm_f32_kernel<EPI><<<grid, 256, 0, s>>>(static_cast<const float*>(A), lda,

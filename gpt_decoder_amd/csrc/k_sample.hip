@@ -252,8 +252,7 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     int32_t* __restrict__ lens, const int32_t* __restrict__ limit,
     int32_t* __restrict__ status, int32_t* __restrict__ hist, int Tb,
     const void* __restrict__ wte,
-    const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x,
-    float* __restrict__ stats) {
+    const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x) {
   __shared__ SampShared sh;
   const int b = blockIdx.x;
   bool active = true;
@@ -269,9 +268,6 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     }
     // inactive row: keep its residual finite; nothing of it is stored
     for (int c = threadIdx.x; c < C; c += blockDim.x) x[(size_t)b * C + c] = 0.f;
-    if (stats)
-      for (int c = threadIdx.x; c < 2 * (C / 32); c += blockDim.x)
-        stats[(size_t)b * 2 * (C / 32) + c] = 0.f;
     return;
   }
   int id;
@@ -307,24 +303,21 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
   }
   if (mode != SAMPLE_ONLY) {
     float* xr = x + (size_t)b * C;
-    float* st = stats ? stats + (size_t)b * 2 * (C / 32) : nullptr;
-    if (dtype == NGPT_BF16) {
+    if (dtype == NGPT_BF16)
       write_embedding((const bf16_t*)wte, (const bf16_t*)wpe, id, len, C, xr);
-      if (st) embed_slice_stats((const bf16_t*)wte + (size_t)id * C, (const bf16_t*)wpe + (size_t)len * C, C, st);
-    } else if (dtype == NGPT_F16) {
+    else if (dtype == NGPT_F16)
       write_embedding((const f16_t*)wte, (const f16_t*)wpe, id, len, C, xr);
-      if (st) embed_slice_stats((const f16_t*)wte + (size_t)id * C, (const f16_t*)wpe + (size_t)len * C, C, st);
-    } else
+    else
       write_embedding((const float*)wte, (const float*)wpe, id, len, C, xr);
   }
 }
 
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p) {
-  void* vals[21] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
+  void* vals[20] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
                     &a.feed_ids, &a.next_ids, &a.tok, &a.pos, &a.lens,
                     &a.limit, &a.status, &a.hist, &a.Tb, &a.wte, &a.wpe, &a.C,
-                    &a.dtype, &a.x, &a.stats};
-  for (int i = 0; i < 21; ++i) a.ptrs[i] = vals[i];
+                    &a.dtype, &a.x};
+  for (int i = 0; i < 20; ++i) a.ptrs[i] = vals[i];
   p->func = reinterpret_cast<void*>(sampler_kernel);
   p->gridDim = dim3(B);
   p->blockDim = dim3(a.mode == FEED_STEP ? 256 : kSampThreads);
@@ -340,7 +333,7 @@ void launch_sampler(const SamplerArgs& a, int B, hipStream_t s) {
                                        a.params, a.feed_ids, a.next_ids, a.tok,
                                        a.pos, a.lens, a.limit, a.status,
                                        a.hist, a.Tb, a.wte, a.wpe, a.C,
-                                       a.dtype, a.x, a.stats);
+                                       a.dtype, a.x);
 }
 
 }  // namespace ngpt

@@ -40,14 +40,7 @@ struct EpiArgs {
   const int32_t* row_b = nullptr;    // row -> sequence (null: identity)
   const int32_t* row_pos = nullptr;  // row -> position; < 0 => inactive row
   int C = 0, H = 0, hs = 0, Tb = 0;
-  // EPI_RESID on the tile path: when set, also the statistics of each new
-  // residual row over every 32-column slice, [M][N/32][2] = (mean, sum of
-  // squared deviations from it), for a LayerNorm applied by the consumer
-  float* stats = nullptr;
 };
-
-// Statistics of rows in 32-column slices: (mean, M2) per slice.
-constexpr int kStatSlice = 32;
 
 // Sampling parameters, resident in device memory so that a captured decode
 // graph picks up changes.
@@ -73,7 +66,7 @@ void launch_embed_prefill(int dtype, const int32_t* ids, int Tmax,
                           const void* wpe, int C, int V, float* x,
                           int32_t* row_b, int32_t* row_pos, int32_t* last_rows,
                           int32_t* last_slot, int32_t* hist, int Tb,
-                          int32_t* status, float* stats, hipStream_t s);
+                          int32_t* status, hipStream_t s);
 
 void launch_embed_decode(int dtype, const int32_t* tok, const int32_t* pos,
                          int B, const void* wte, const void* wpe, int C, int V,
@@ -93,10 +86,6 @@ struct LnArgs {
   const void* w = nullptr;
   const void* b = nullptr;
   void* h = nullptr;
-  // When set (16-bit tile path): the rows' 32-column slice statistics
-  // (EpiArgs::stats of the producer); the LayerNorm is then applied as the
-  // tile GEMM loads x, with no h buffer and no LayerNorm launch.
-  const float* stats = nullptr;
 };
 
 // acc = A[M][K] W[N][K]^T, then the epilogue.  A and W are dtype.  With
@@ -165,8 +154,7 @@ struct SamplerArgs {
   int C = 0;
   int dtype = 0;
   float* x = nullptr;
-  float* stats = nullptr;   // slice statistics of the written embedding rows
-  void* ptrs[21] = {};
+  void* ptrs[20] = {};
 };
 // Fill a kernel-node description for B rows; `a` must outlive its use.
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
