@@ -25,6 +25,8 @@ NGPT_E_CONTEXT = -5
 NGPT_E_HIP = -6
 NGPT_E_DEVICE = -7
 NGPT_E_TIMEOUT = -8
+NGPT_E_PAGE = -9
+NGPT_PAGE_TOKENS = 64
 NGPT_F32 = 0
 NGPT_BF16 = 1
 NGPT_F16 = 2
@@ -61,7 +63,8 @@ class Weights(ctypes.Structure):
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("lens", ctypes.c_void_p), ("limit", ctypes.c_void_p),
-                ("batch", ctypes.c_int32)]
+                ("batch", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -80,6 +83,9 @@ def lib():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.ngpt_kv_bytes.argtypes = [ctypes.POINTER(Config), i32]
     L.ngpt_kv_bytes.restype = sz
+    L.ngpt_kv_pool_bytes.argtypes = [ctypes.POINTER(Config), i32]
+    L.ngpt_kv_pool_bytes.restype = sz
+    L.ngpt_kv_map.argtypes = [vp, ctypes.POINTER(KV), i32, i32, i32, vp]
     L.ngpt_workspace_bytes.argtypes = [ctypes.POINTER(Config)]
     L.ngpt_workspace_bytes.restype = sz
     L.ngpt_check_config.argtypes = [ctypes.POINTER(Config)]
@@ -142,6 +148,10 @@ def kv_bytes(cfg: Config, batch: int) -> int:
     return int(lib().ngpt_kv_bytes(ctypes.byref(cfg), batch))
 
 
+def kv_pool_bytes(cfg: Config, num_pages: int) -> int:
+    return int(lib().ngpt_kv_pool_bytes(ctypes.byref(cfg), num_pages))
+
+
 def workspace_bytes(cfg: Config) -> int:
     return int(lib().ngpt_workspace_bytes(ctypes.byref(cfg)))
 
@@ -155,11 +165,16 @@ def _ptr(t) -> int:
 
 
 class KVCache:
-    """Caller-owned KV cache: K and V [L][B][H][Tb][hs] plus lens/limit."""
+    """Caller-owned KV cache plus lens/limit.
 
-    def __init__(self, cfg: Config, batch: int, device="cuda"):
+    Contiguous (``num_pages`` None): K and V [L][B][H][Tb][hs].  Paged: K and
+    V pools [L][num_pages][H][64][hs] and a block table [B][ceil(Tb/64)] of
+    page ids, every block unmapped (-1) until mapped with Model.kv_map."""
+
+    def __init__(self, cfg: Config, batch: int, device="cuda", num_pages=None):
         import torch
-        nbytes = kv_bytes(cfg, batch)
+        paged = num_pages is not None
+        nbytes = kv_pool_bytes(cfg, num_pages) if paged else kv_bytes(cfg, batch)
         if nbytes == 0 and cfg.n_layer > 0:
             raise NgptError(NGPT_E_CONFIG, "invalid config for the KV cache")
         n = max(nbytes, 16)
@@ -168,8 +183,12 @@ class KVCache:
         self.lens = torch.zeros(batch, dtype=torch.int32, device=device)
         self.limit = torch.zeros(batch, dtype=torch.int32, device=device)
         self.batch = batch
+        self.num_pages = num_pages
+        self.nblk = (cfg.block_size + NGPT_PAGE_TOKENS - 1) // NGPT_PAGE_TOKENS
+        self.table = (torch.full((batch, self.nblk), -1, dtype=torch.int32, device=device)
+                      if paged else None)
         self.struct = KV(_ptr(self.k), _ptr(self.v), _ptr(self.lens),
-                         _ptr(self.limit), batch)
+                         _ptr(self.limit), batch, int(num_pages or 0), _ptr(self.table))
 
 
 class Model:
@@ -245,8 +264,8 @@ class Model:
         if rc != NGPT_OK:
             raise NgptError(rc, lib().ngpt_last_error(self.h).decode())
 
-    def new_kv(self, batch: int) -> KVCache:
-        return KVCache(self.cfg, batch, self.device)
+    def new_kv(self, batch: int, num_pages=None) -> KVCache:
+        return KVCache(self.cfg, batch, self.device, num_pages)
 
     # -- the C calls ---------------------------------------------------------
     def set_sampling(self, temperature=1.0, top_k=0, greedy=False):
@@ -314,6 +333,14 @@ class Model:
             self.h, ctypes.byref(kv.struct), a.ctypes.data_as(ctypes.c_void_p),
             lens_a, B, Tmax, _ptr(logits), _ptr(losses), _ptr(mean)))
         return logits, losses, mean
+
+    def kv_map(self, kv: KVCache, slot: int, first_block: int, pages):
+        """Map blocks first_block.. of row ``slot`` of a paged cache to the
+        host page ids ``pages`` (-1 unmaps)."""
+        pg = self._host_i32(pages)
+        self._check(lib().ngpt_kv_map(self.h, ctypes.byref(kv.struct), int(slot),
+                                      int(first_block), len(pg),
+                                      pg.ctypes.data_as(ctypes.c_void_p)))
 
     def retire(self, kv: KVCache, slots):
         sl = self._host_i32(slots)

@@ -58,14 +58,27 @@ __global__ void window_ids_kernel(SlotList sl, const int32_t* hist, int Tb,
 }
 
 // Report and clear the kernel-side flags: bit 2 a one-launch decode wait
-// gave up, bit 1 invalid input (an id out of range, or a greedy row with no
-// finite maximum).  `out` is device memory or device-writable host memory.
+// gave up, bit 4 a cache write into an unmapped block of a paged cache, bit
+// 1 invalid input (an id out of range, or a greedy row with no finite
+// maximum).  `out` is device memory or device-writable host memory.
 __global__ void read_status_kernel(int32_t* status, int32_t* out) {
   if (threadIdx.x == 0) {
     const int32_t v = status[0];
-    out[0] = (v & 2) ? NGPT_E_TIMEOUT : v ? NGPT_E_DEVICE : NGPT_OK;
+    out[0] = (v & 2) ? NGPT_E_TIMEOUT : (v & 4) ? NGPT_E_PAGE : v ? NGPT_E_DEVICE : NGPT_OK;
     status[0] = 0;
   }
+}
+
+// Block-table entries of one row of a paged cache, from a kernel argument
+// (so the call needs no host staging and no wait).
+constexpr int kMaxMapBlocks = (4096 + NGPT_PAGE_TOKENS - 1) / NGPT_PAGE_TOKENS;
+struct PageArgs {
+  int32_t count;
+  int32_t pages[kMaxMapBlocks];
+};
+__global__ void set_pages_kernel(int32_t* dst, PageArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.count) dst[i] = a.pages[i];
 }
 
 // Sampling parameters written on the stream from a kernel argument, so that
@@ -106,6 +119,8 @@ struct GraphSlot {
   void* v = nullptr;
   int32_t* lens = nullptr;
   int32_t* limit = nullptr;
+  int32_t* table = nullptr;
+  int32_t num_pages = 0;
   int32_t batch = 0;
   int32_t wait_limit = 0;
   const void* arg_in = nullptr;   // uniforms (step) or feed ids (feed)
@@ -124,6 +139,7 @@ const char* status_name(int s) {
     case NGPT_E_HIP: return "NGPT_E_HIP";
     case NGPT_E_DEVICE: return "NGPT_E_DEVICE";
     case NGPT_E_TIMEOUT: return "NGPT_E_TIMEOUT";
+    case NGPT_E_PAGE: return "NGPT_E_PAGE";
     default: return "NGPT_E_UNKNOWN";
   }
 }
@@ -270,6 +286,13 @@ size_t ngpt_kv_bytes(const ngpt_config* cfg, int32_t batch) {
   if (check_config(cfg, nullptr) != NGPT_OK || batch < 1) return 0;
   const size_t es = cfg->dtype == NGPT_F32 ? 4 : 2;
   return (size_t)cfg->n_layer * batch * cfg->n_head * cfg->block_size *
+         (cfg->n_embd / cfg->n_head) * es;
+}
+
+size_t ngpt_kv_pool_bytes(const ngpt_config* cfg, int32_t num_pages) {
+  if (check_config(cfg, nullptr) != NGPT_OK || num_pages < 1) return 0;
+  const size_t es = cfg->dtype == NGPT_F32 ? 4 : 2;
+  return (size_t)cfg->n_layer * num_pages * cfg->n_head * NGPT_PAGE_TOKENS *
          (cfg->n_embd / cfg->n_head) * es;
 }
 
@@ -539,17 +562,39 @@ static int check_kv(ngpt_model* m, const ngpt_kv* kv) {
   if (kv->batch > m->cfg.max_batch) return fail(m, NGPT_E_SIZE, "kv batch > max_batch");
   if (misaligned(kv->k) || misaligned(kv->v))
     return fail(m, NGPT_E_ARG, "kv arrays must be 16-byte aligned");
+  if (kv->block_table && kv->num_pages < 1)
+    return fail(m, NGPT_E_ARG, "a paged kv needs num_pages >= 1");
   return NGPT_OK;
 }
 
 static bool same_kv(const ngpt_kv& a, const ngpt_kv& b) {
   return a.k == b.k && a.v == b.v && a.lens == b.lens && a.limit == b.limit &&
-         a.batch == b.batch;
+         a.batch == b.batch && a.block_table == b.block_table &&
+         (!a.block_table || a.num_pages == b.num_pages);
 }
 
-static void* layer_cache(const ngpt_model* m, void* base, int l, int kvB) {
-  return static_cast<char*>(base) +
-         (size_t)l * kvB * m->H * m->Tb * m->hs * m->esz;
+// One layer of the K or V array: [batch][H][Tb][hs] contiguous, or
+// [num_pages][H][64][hs] paged.
+static void* layer_cache(const ngpt_model* m, void* base, int l, const ngpt_kv* kv) {
+  const size_t rows = kv->block_table ? (size_t)kv->num_pages * m->H * NGPT_PAGE_TOKENS
+                                      : (size_t)kv->batch * m->H * m->Tb;
+  return static_cast<char*>(base) + (size_t)l * rows * m->hs * m->esz;
+}
+
+static KvMap kv_map(const ngpt_model* m, const ngpt_kv* kv) {
+  KvMap k;
+  k.table = kv->block_table;
+  k.nblk = (m->Tb + NGPT_PAGE_TOKENS - 1) / NGPT_PAGE_TOKENS;
+  k.npages = kv->block_table ? kv->num_pages : 0;
+  k.H = m->H;
+  k.Tb = m->Tb;
+  return k;
+}
+
+// Whether a decode step of this cache runs as the one-launch kernel (batch
+// 1, contiguous cache, a supported shape).
+static bool one_launch(const ngpt_model* m, const ngpt_kv* kv) {
+  return m->persist && kv->batch == 1 && !kv->block_table;
 }
 
 // Which rows a launch of the prefill sequence processes, and how the host
@@ -686,17 +731,19 @@ static void enqueue_blocks(ngpt_model* m, ngpt_kv* kv, const int32_t* ids, int T
   launch_embed_prefill(dt, ids, Tmax, map, M, m->wte, m->wpe, C, m->V, m->x,
                        m->row_b, m->row_pos, m->last_rows, m->last_slot, m->hist,
                        m->Tb, m->status, s);
+  const KvMap kvm = kv_map(m, kv);
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
-    void* kl = layer_cache(m, kv->k, l, kv->batch);
-    void* vl = layer_cache(m, kv->v, l, kv->batch);
+    void* kl = layer_cache(m, kv->k, l, kv);
+    void* vl = layer_cache(m, kv->v, l, kv);
     const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = m->row_b; eq.row_pos = m->row_pos;
+    eq.kv = kvm; eq.status = m->status;
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
     launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, M, 3 * C, C, eq, s);
-    launch_attn_prefill(dt, m->q, C, kl, vl, map, pl.maxlen, m->H, m->hs, m->Tb,
+    launch_attn_prefill(dt, m->q, C, kl, vl, kvm, map, pl.maxlen, m->H, m->hs, m->Tb,
                         m->y, C, m->ppart, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
@@ -843,6 +890,30 @@ int ngpt_retire(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, int32_t n) {
   return NGPT_OK;
 }
 
+int ngpt_kv_map(ngpt_model* m, ngpt_kv* kv, int32_t slot, int32_t first_block,
+                int32_t count, const int32_t* pages) {
+  if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
+  int rc = check_kv(m, kv);
+  if (rc != NGPT_OK) return rc;
+  if (!kv->block_table) return fail(m, NGPT_E_ARG, "kv is not paged (block_table is NULL)");
+  if (!pages) return fail(m, NGPT_E_ARG, "pages is NULL");
+  const int nblk = (m->Tb + NGPT_PAGE_TOKENS - 1) / NGPT_PAGE_TOKENS;
+  if (slot < 0 || slot >= kv->batch) return fail(m, NGPT_E_RANGE, "slot outside [0, kv->batch)");
+  if (first_block < 0 || count < 1 || first_block + count > nblk)
+    return fail(m, NGPT_E_RANGE, "blocks outside [0, ceil(block_size / 64))");
+  PageArgs a{};
+  a.count = count;
+  for (int i = 0; i < count; ++i) {
+    if (pages[i] < -1 || pages[i] >= kv->num_pages)
+      return fail(m, NGPT_E_RANGE, "page id outside [-1, num_pages)");
+    a.pages[i] = pages[i];
+  }
+  set_pages_kernel<<<1, kMaxMapBlocks, 0, m->stream>>>(
+      kv->block_table + (size_t)slot * nblk + first_block, a);
+  HIP_TRY(m, hipGetLastError());
+  return NGPT_OK;
+}
+
 int ngpt_slide(ngpt_model* m, ngpt_kv* kv, const int32_t* slots, int32_t n,
                const int32_t* next_ids) {
   if (!m) return fail(nullptr, NGPT_E_ARG, "model is NULL");
@@ -911,22 +982,24 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
 
 static void enqueue_decode_forward(ngpt_model* m, const ngpt_kv* kv, hipStream_t s) {
   const int Bk = kv->batch, C = m->C, dt = m->cfg.dtype;
-  if (m->persist && Bk == 1) {
+  if (one_launch(m, kv)) {
     launch_decode_persistent(persist_args(m, kv), m->persist_grid, s);
     return;
   }
+  const KvMap kvm = kv_map(m, kv);
   for (int l = 0; l < m->L; ++l) {
     const ngpt_layer_weights& w = m->layers[l];
-    void* kl = layer_cache(m, kv->k, l, Bk);
-    void* vl = layer_cache(m, kv->v, l, Bk);
+    void* kl = layer_cache(m, kv->k, l, kv);
+    void* vl = layer_cache(m, kv->v, l, kv);
     const LnArgs ln1{m->x, C, w.ln1_w, w.ln1_b, m->h};
     EpiArgs eq;
     eq.bias = w.attn_b; eq.out = m->q; eq.ldo = C; eq.kc = kl; eq.vc = vl;
     eq.row_b = nullptr; eq.row_pos = m->pos;
+    eq.kv = kvm; eq.status = m->status;
     eq.C = C; eq.H = m->H; eq.hs = m->hs; eq.Tb = m->Tb;
     launch_linear(dt, EPI_QKV, nullptr, C, &ln1, w.attn_w, Bk, 3 * C, C, eq, s);
     const bool fused = decode_fused_proj(Bk);
-    launch_attn_decode(dt, m->q, kl, vl, m->pos, Bk, m->H, m->hs, m->Tb,
+    launch_attn_decode(dt, m->q, kl, vl, kvm, m->pos, Bk, m->H, m->hs, m->Tb,
                        m->part, m->y, !fused, s);
     EpiArgs ep;
     ep.bias = w.attnproj_b; ep.out = m->x; ep.ldo = C;
@@ -1004,6 +1077,7 @@ static int capture(ngpt_model* m, GraphSlot& g, const ngpt_kv* kv, int mode,
   }
   g.graph = graph; g.exec = exec; g.head = root;
   g.k = kv->k; g.v = kv->v; g.lens = kv->lens; g.limit = kv->limit;
+  g.table = kv->block_table; g.num_pages = kv->num_pages;
   g.batch = kv->batch; g.arg_in = arg_in; g.arg_out = arg_out;
   g.wait_limit = m->h_wait_limit;
   g.head_args = a;
@@ -1023,8 +1097,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   if (!any) return fail(m, NGPT_E_CONTEXT, "no sequence can take another token");
   // Greedy batch-1 step after a one-launch forward: the launch picks its own
   // token from the candidates the previous one left, no head node.
-  if (mode == SAMPLE_STEP && m->h_params.greedy && m->persist && kv->batch == 1 &&
-      m->cand_ok) {
+  if (mode == SAMPLE_STEP && m->h_params.greedy && one_launch(m, kv) && m->cand_ok) {
     PersistArgs a = persist_args(m, kv);
     a.fused = 1;
     a.next_ids = arg_out;
@@ -1035,6 +1108,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   }
   const bool same = g.exec && g.k == kv->k && g.v == kv->v &&
                     g.lens == kv->lens && g.limit == kv->limit &&
+                    g.table == kv->block_table && g.num_pages == kv->num_pages &&
                     g.batch == kv->batch && g.wait_limit == m->h_wait_limit;
   if (!same) {
     rc = capture(m, g, kv, mode, arg_in, arg_out);
@@ -1049,7 +1123,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
     g.arg_out = arg_out;
   }
   HIP_TRY(m, hipGraphLaunch(g.exec, m->stream));
-  m->cand_ok = m->persist && kv->batch == 1;
+  m->cand_ok = one_launch(m, kv);
   for (int b = 0; b < kv->batch; ++b)
     if (m->h_lens[b] < m->h_limit[b]) ++m->h_lens[b];
   return NGPT_OK;

@@ -52,7 +52,7 @@ constexpr int kPrefillKch = 8;   // key tiles per chunk when a prefill tile is s
 template <class T, int HS>
 __global__ __launch_bounds__(256) void attn_prefill_mfma(
     const T* __restrict__ q, int ldq, const T* __restrict__ kc,
-    const T* __restrict__ vc, RowMap map, int H, int Tb, float scale,
+    const T* __restrict__ vc, KvMap kvm, RowMap map, int H, int Tb, float scale,
     T* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part) {
   typedef typename Half16<T>::vec8 vec8;
   constexpr int KT = 64;             // keys per tile
@@ -84,8 +84,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const int kend = past + len;                    // keys in the cache
   const size_t row0 = (size_t)map.off[b];
   const int slot = map.slot[b];
-  const T* kbase = kc + ((size_t)slot * H + h) * Tb * HS;
-  const T* vbase = vc + ((size_t)slot * H + h) * Tb * HS;
+  const int64_t hoff = (int64_t)h * kv_hstride(kvm);
 
   // Q^T operand: column = this lane's query, K-values = dims 8g.. (+32 kk)
   vec8 qf[NKK];
@@ -107,19 +106,22 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
   // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
   // S tiles are in flight in registers.  The loads are range-checked buffer
-  // loads issued on every path: keys at or past len (whose cache rows may
-  // hold anything) and tiles past the block read zeros.
+  // loads issued on every path, through a resource spanning the tile's 64
+  // cache rows (one block): keys at or past len (whose cache rows may hold
+  // anything), tiles past the last key and unmapped blocks read zeros.
   constexpr int ITEMS = (KT / 2) * (HS / 8);
   constexpr int IPT = (ITEMS + 255) / 256;
   constexpr int S = 4;
   constexpr uint32_t kOut = 0x80000000u;
-  const uint32_t blk = (uint32_t)Tb * HS * 2u;
-  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(kbase), (short)0, (int)blk, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(vbase), (short)0, (int)blk, 0x00020000);
   uint4 rk[S][IPT][2], rv[S][IPT][2];
   auto load_tile = [&](int st, int k0) {
+    const int64_t bb = k0 < kend ? kv_block_base(kvm, slot, k0 / KT) : -1;
+    const size_t r0 = bb < 0 ? 0 : (size_t)(bb + hoff) * HS;
+    const int nrec = bb < 0 ? 0 : KT * HS * 2;
+    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(kc + r0), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(vc + r0), (short)0, nrec, 0x00020000);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int c = tid + it * 256;
@@ -127,7 +129,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         const int key = k0 + 2 * kp + e2;
-        const uint32_t off = (c < ITEMS && key < kend) ? ((uint32_t)key * HS + d0) * 2u : kOut;
+        const uint32_t off =
+            (c < ITEMS && key < kend) ? ((uint32_t)(key - k0) * HS + d0) * 2u : kOut;
         rk[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, off, 0, 0));
         rv[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, off, 0, 0));
       }
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_prefill_merge(
 template <class T, int HS>
 __global__ __launch_bounds__(64) void attn_prefill_simt(
     const T* __restrict__ q, int ldq, const T* __restrict__ kc,
-    const T* __restrict__ vc, RowMap map, int H, int Tb, float scale,
+    const T* __restrict__ vc, KvMap kvm, RowMap map, int H, int Tb, float scale,
     T* __restrict__ y, int ldy) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int len = map.off[b + 1] - map.off[b];
@@ -293,8 +296,8 @@ __global__ __launch_bounds__(64) void attn_prefill_simt(
   if (i >= len) return;
   const int t = map.past[b] + i;        // position: sees keys 0 .. t
   const size_t row = (size_t)map.off[b] + i;
-  const T* kbase = kc + ((size_t)map.slot[b] * H + h) * Tb * HS;
-  const T* vbase = vc + ((size_t)map.slot[b] * H + h) * Tb * HS;
+  const int slot = map.slot[b];
+  const int64_t hoff = (int64_t)h * kv_hstride(kvm);
   float qv[HS], acc[HS];
 #pragma unroll
   for (int d = 0; d < HS; ++d) {
@@ -302,18 +305,23 @@ __global__ __launch_bounds__(64) void attn_prefill_simt(
     acc[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  int64_t bb = -1;
   for (int u = 0; u <= t; ++u) {
-    const T* kr = kbase + (size_t)u * HS;
+    if (u % kPageTokens == 0) bb = kv_block_base(kvm, slot, u / kPageTokens);
+    // an unmapped block reads as zeros
+    const bool ok = bb >= 0;
+    const size_t kr0 = ok ? (size_t)(bb + hoff + u % kPageTokens) * HS : 0;
+    const T* kr = kc + kr0;
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < HS; ++d) s = fmaf(qv[d], to_f32(kr[d]), s);
+    for (int d = 0; d < HS; ++d) s = fmaf(qv[d], ok ? to_f32(kr[d]) : 0.f, s);
     const float m_new = fmaxf(m, s);
     const float alpha = expf(m - m_new);
     const float p = expf(s - m_new);
     l = l * alpha + p;
-    const T* vr = vbase + (size_t)u * HS;
+    const T* vr = vc + kr0;
 #pragma unroll
-    for (int d = 0; d < HS; ++d) acc[d] = acc[d] * alpha + p * to_f32(vr[d]);
+    for (int d = 0; d < HS; ++d) acc[d] = acc[d] * alpha + p * (ok ? to_f32(vr[d]) : 0.f);
     m = m_new;
   }
   const float inv = 1.f / l;
@@ -333,12 +341,13 @@ constexpr int kDecChunk = 64;
 template <class T, int HS>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-    const int32_t* __restrict__ pos, int H, int Tb, int nchunk, float scale,
+    KvMap kvm, const int32_t* __restrict__ pos, int H, int Tb, int nchunk, float scale,
     float* __restrict__ part) {
   constexpr int LPK = HS / 8;          // lanes per key
   constexpr int KPP = 64 / LPK;        // keys per wavefront pass
   constexpr int KPW = kDecChunk / 4;   // keys per wavefront
   constexpr int PS = HS + 2;           // partial record: m, l, o[HS]
+  static_assert(kPageTokens % KPW == 0, "a wavefront's keys must lie in one cache block");
   __shared__ float sw[4][PS];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -350,24 +359,28 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int sub = lane % LPK;   // which 8 dims
   const int kgrp = lane / LPK;  // key slot within a pass
   const float sl2 = scale * kLog2e;
-  const T* kbase = kc + ((size_t)b * H + h) * Tb * HS;
-  const T* vbase = vc + ((size_t)b * H + h) * Tb * HS;
+  // the wavefront's keys kw .. kw + KPW - 1 lie in one cache block (KPW
+  // divides the block's 64 positions); an unmapped block reads as zeros
+  const int kw = chunk * kDecChunk + wave * KPW;
+  const int64_t bb = kw <= p ? kv_block_base(kvm, b, kw / kPageTokens) : -1;
+  const size_t r0 = bb < 0 ? 0 : (size_t)(bb + (int64_t)h * kv_hstride(kvm)) * HS;
+  const T* kbase = kc + r0;
+  const T* vbase = vc + r0;
 
   // issue every K/V load of this lane first, then the query
-  const int kw = chunk * kDecChunk + wave * KPW;
   float kf[KPW / KPP][8], vf[KPW / KPP][8];
 #pragma unroll
   for (int pass = 0; pass < KPW / KPP; ++pass) {
     const int u = kw + pass * KPP + kgrp;
-    if (u <= p) {
+    if (u <= p && bb >= 0) {
       if constexpr (sizeof(T) == 2) {
-        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(kbase + (size_t)u * HS + sub * 8), kf[pass]);
-        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(vbase + (size_t)u * HS + sub * 8), vf[pass]);
+        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(kbase + (size_t)(u % kPageTokens) * HS + sub * 8), kf[pass]);
+        Half16<T>::unpack8(*reinterpret_cast<const uint4*>(vbase + (size_t)(u % kPageTokens) * HS + sub * 8), vf[pass]);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          kf[pass][j] = to_f32(kbase[(size_t)u * HS + sub * 8 + j]);
-          vf[pass][j] = to_f32(vbase[(size_t)u * HS + sub * 8 + j]);
+          kf[pass][j] = to_f32(kbase[(size_t)(u % kPageTokens) * HS + sub * 8 + j]);
+          vf[pass][j] = to_f32(vbase[(size_t)(u % kPageTokens) * HS + sub * 8 + j]);
         }
       }
     } else {
@@ -473,7 +486,8 @@ int attn_prefill_split_chunks(int Tb) { return ((Tb + 63) / 64 + kPrefillKch - 1
 
 template <class T>
 static void launch_attn_prefill_h(const T* q, int ldq, const T* kc, const T* vc,
-                                  const RowMap& map, int maxlen, int H, int hs, int Tb,
+                                  const KvMap& kv, const RowMap& map, int maxlen, int H,
+                                  int hs, int Tb,
                                   T* y, int ldy, float* part, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hs);
   const int ntiles = (maxlen + 63) / 64;
@@ -485,10 +499,10 @@ static void launch_attn_prefill_h(const T* q, int ldq, const T* kc, const T* vc,
   const int nsplit = split ? (nkt_max + kPrefillKch - 1) / kPrefillKch : 1;
   const dim3 grid(ntiles * nsplit, H, map.B);
   if (hs == 64)
-    attn_prefill_mfma<T, 64><<<grid, 256, 0, s>>>(q, ldq, kc, vc, map, H, Tb, scale, y, ldy,
+    attn_prefill_mfma<T, 64><<<grid, 256, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
                                                    kch, nsplit, part);
   else
-    attn_prefill_mfma<T, 32><<<grid, 256, 0, s>>>(q, ldq, kc, vc, map, H, Tb, scale, y, ldy,
+    attn_prefill_mfma<T, 32><<<grid, 256, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
                                                    kch, nsplit, part);
   if (split) {
     // rows of single-chunk tiles need no merge: start at the first tile
@@ -507,14 +521,15 @@ static void launch_attn_prefill_h(const T* q, int ldq, const T* kc, const T* vc,
 }
 
 void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
-                         const void* vc, const RowMap& map, int maxlen, int H,
-                         int hs, int Tb, void* y, int ldy, float* part, hipStream_t s) {
+                         const void* vc, const KvMap& kv, const RowMap& map, int maxlen,
+                         int H, int hs, int Tb, void* y, int ldy, float* part,
+                         hipStream_t s) {
   if (dtype == NGPT_BF16) {
     launch_attn_prefill_h<bf16_t>((const bf16_t*)q, ldq, (const bf16_t*)kc, (const bf16_t*)vc,
-                                  map, maxlen, H, hs, Tb, (bf16_t*)y, ldy, part, s);
+                                  kv, map, maxlen, H, hs, Tb, (bf16_t*)y, ldy, part, s);
   } else if (dtype == NGPT_F16) {
     launch_attn_prefill_h<f16_t>((const f16_t*)q, ldq, (const f16_t*)kc, (const f16_t*)vc,
-                                 map, maxlen, H, hs, Tb, (f16_t*)y, ldy, part, s);
+                                 kv, map, maxlen, H, hs, Tb, (f16_t*)y, ldy, part, s);
   } else {
     const float scale = 1.0f / sqrtf((float)hs);
     const int ntiles = (maxlen + 63) / 64;
@@ -522,10 +537,10 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
     const float* qq = (const float*)q;
     if (hs == 64)
       attn_prefill_simt<float, 64><<<grid, 64, 0, s>>>(qq, ldq, (const float*)kc,
-          (const float*)vc, map, H, Tb, scale, (float*)y, ldy);
+          (const float*)vc, kv, map, H, Tb, scale, (float*)y, ldy);
     else
       attn_prefill_simt<float, 32><<<grid, 64, 0, s>>>(qq, ldq, (const float*)kc,
-          (const float*)vc, map, H, Tb, scale, (float*)y, ldy);
+          (const float*)vc, kv, map, H, Tb, scale, (float*)y, ldy);
   }
 }
 
@@ -534,34 +549,34 @@ int attn_decode_chunks(int Tb) { return (Tb + kDecChunk - 1) / kDecChunk; }
 int attn_decode_chunk_keys() { return kDecChunk; }
 
 template <class T>
-static void launch_attn_decode_t(const T* q, const T* kc, const T* vc, const int32_t* pos,
-                                 int B, int H, int hs, int Tb, float* part, T* y,
-                                 bool merge_into_y, hipStream_t s) {
+static void launch_attn_decode_t(const T* q, const T* kc, const T* vc, const KvMap& kv,
+                                 const int32_t* pos, int B, int H, int hs, int Tb,
+                                 float* part, T* y, bool merge_into_y, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hs);
   const int nchunk = attn_decode_chunks(Tb);
   const dim3 grid(nchunk, H, B), cgrid(H, B);
   if (hs == 64) {
-    attn_decode_kernel<T, 64><<<grid, 256, 0, s>>>(q, kc, vc, pos, H, Tb, nchunk, scale, part);
+    attn_decode_kernel<T, 64><<<grid, 256, 0, s>>>(q, kc, vc, kv, pos, H, Tb, nchunk, scale, part);
     if (merge_into_y) attn_decode_combine<T, 64><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, y);
   } else {
-    attn_decode_kernel<T, 32><<<grid, 256, 0, s>>>(q, kc, vc, pos, H, Tb, nchunk, scale, part);
+    attn_decode_kernel<T, 32><<<grid, 256, 0, s>>>(q, kc, vc, kv, pos, H, Tb, nchunk, scale, part);
     if (merge_into_y) attn_decode_combine<T, 32><<<cgrid, 64, 0, s>>>(part, pos, H, nchunk, y);
   }
 }
 
 void launch_attn_decode(int dtype, const void* q, const void* kc,
-                        const void* vc, const int32_t* pos, int B, int H,
+                        const void* vc, const KvMap& kv, const int32_t* pos, int B, int H,
                         int hs, int Tb, float* part, void* y,
                         bool merge_into_y, hipStream_t s) {
   if (dtype == NGPT_BF16) {
-    launch_attn_decode_t<bf16_t>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, pos,
-                                 B, H, hs, Tb, part, (bf16_t*)y, merge_into_y, s);
+    launch_attn_decode_t<bf16_t>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, kv,
+                                 pos, B, H, hs, Tb, part, (bf16_t*)y, merge_into_y, s);
   } else if (dtype == NGPT_F16) {
-    launch_attn_decode_t<f16_t>((const f16_t*)q, (const f16_t*)kc, (const f16_t*)vc, pos,
-                                B, H, hs, Tb, part, (f16_t*)y, merge_into_y, s);
+    launch_attn_decode_t<f16_t>((const f16_t*)q, (const f16_t*)kc, (const f16_t*)vc, kv,
+                                pos, B, H, hs, Tb, part, (f16_t*)y, merge_into_y, s);
   } else {
-    launch_attn_decode_t<float>((const float*)q, (const float*)kc, (const float*)vc, pos,
-                                B, H, hs, Tb, part, (float*)y, merge_into_y, s);
+    launch_attn_decode_t<float>((const float*)q, (const float*)kc, (const float*)vc, kv,
+                                pos, B, H, hs, Tb, part, (float*)y, merge_into_y, s);
   }
 }
 

@@ -49,10 +49,16 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
       const int p = e.row_pos[r];
       if (p < 0) return;
       const int b = e.row_b ? e.row_b[r] : r;
+      const int64_t base = kv_block_base(e.kv, b, p / kPageTokens);
+      if (base < 0) {   // unmapped block of a paged cache
+        if (e.status) atomicOr(e.status, 4);
+        return;
+      }
       const int h = c / e.hs;
       const int d = c - h * e.hs;
       T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
-      cache[(((size_t)b * e.H + h) * e.Tb + p) * e.hs + d] = from_f32<T>(v);
+      cache[(size_t)(base + (int64_t)h * kv_hstride(e.kv) + p % kPageTokens) * e.hs + d] =
+          from_f32<T>(v);
     }
   }
 }
@@ -201,15 +207,20 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   // otherwise column (l % 16) at rows 4 * (l / 16) + i)
   auto out_row = [&](int i) { return m0 + wm * WM + i * 16 + (lane & 15); };
   auto out_col = [&](int j) { return n0 + wn * WN + j * 16 + (lane >> 4) * 4; };
-  int rpos[TM], rseq[TM];
+  // QKV: cache row (of hs elements, head 0) of each output row's position,
+  // -1 for inactive rows and unmapped blocks (the latter flagged)
+  int64_t rrow[TM];
   constexpr bool kPreRes = (EPI == EPI_RESID) && TM * TN * 4 <= 16;
   float res[kPreRes ? TM : 1][kPreRes ? TN : 1][4];
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = min(out_row(i), M - 1);
-      rpos[i] = e.row_pos[row];
-      rseq[i] = e.row_b ? e.row_b[row] : row;
+      const int p = e.row_pos[row];
+      const int sq = e.row_b ? e.row_b[row] : row;
+      const int64_t base = p >= 0 ? kv_block_base(e.kv, sq, p / kPageTokens) : -1;
+      if (p >= 0 && base < 0 && e.status) atomicOr(e.status, 4);
+      rrow[i] = base < 0 ? -1 : base + p % kPageTokens;
     }
   }
   if constexpr (kPreRes) {
@@ -276,6 +287,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
       const int which = col / e.C;
       const int c = col - which * e.C;
       const int hh = c / e.hs, d = c - hh * e.hs;
+      const int64_t hoff = (int64_t)hh * kv_hstride(e.kv);
       T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -286,9 +298,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         const uint2 packed = pack4<T>(v);
         if (which == 0) {
           *reinterpret_cast<uint2*>(static_cast<T*>(e.out) + (size_t)row * e.ldo + c) = packed;
-        } else if (rpos[i] >= 0) {
-          *reinterpret_cast<uint2*>(
-              cache + (((size_t)rseq[i] * e.H + hh) * e.Tb + rpos[i]) * e.hs + d) = packed;
+        } else if (rrow[i] >= 0) {
+          *reinterpret_cast<uint2*>(cache + (size_t)(rrow[i] + hoff) * e.hs + d) = packed;
         }
       }
     }

@@ -22,6 +22,32 @@ struct RowMap {
   int32_t past[NGPT_MAX_BATCH];
 };
 
+// Where one layer's cache keeps position t of sequence b, head h: the row
+// (of hs elements) block_base(b, t / 64) + h * hstride + t % 64.
+//  * contiguous layout [batch][H][Tb][hs] (table == null):
+//    block_base = b * H * Tb + 64 * (t / 64), hstride = Tb;
+//  * paged layout [pages][H][64][hs]: block t / 64 of sequence b lives in
+//    page table[b * nblk + t / 64], block_base = page * H * 64, hstride = 64.
+//    A page id outside [0, npages) is an unmapped block.
+struct KvMap {
+  const int32_t* table = nullptr;
+  int nblk = 0;     // table row stride: blocks per sequence, ceil(Tb / 64)
+  int npages = 0;
+  int H = 0, Tb = 0;
+};
+
+constexpr int kPageTokens = NGPT_PAGE_TOKENS;
+
+// First row of block `blk` of sequence b (head 0); -1 when unmapped.
+__device__ __forceinline__ int64_t kv_block_base(const KvMap& k, int b, int blk) {
+  if (!k.table) return (int64_t)b * k.H * k.Tb + (int64_t)blk * kPageTokens;
+  const int pg = k.table[b * k.nblk + blk];
+  return (uint32_t)pg < (uint32_t)k.npages ? (int64_t)pg * k.H * kPageTokens : -1;
+}
+__device__ __forceinline__ int kv_hstride(const KvMap& k) {
+  return k.table ? kPageTokens : k.Tb;
+}
+
 // Linear-layer epilogues (what happens to acc = A W^T for row r, column n).
 enum Epi {
   EPI_GELU = 1,    // out[r][n] = GELU(acc + bias)                (dtype)
@@ -34,9 +60,12 @@ struct EpiArgs {
   const void* bias = nullptr;     // [N] dtype or null
   void* out = nullptr;
   int ldo = 0;
-  // EPI_QKV: this layer's cache, each [batch][H][Tb][hs]
+  // EPI_QKV: this layer's cache (addressed through kv); a position whose
+  // block is unmapped is not written and sets bit 4 of *status
   void* kc = nullptr;
   void* vc = nullptr;
+  KvMap kv;
+  int32_t* status = nullptr;
   const int32_t* row_b = nullptr;    // row -> sequence (null: identity)
   const int32_t* row_pos = nullptr;  // row -> position; < 0 => inactive row
   int C = 0, H = 0, hs = 0, Tb = 0;
@@ -97,8 +126,9 @@ void launch_linear(int dtype, int epi, const void* A, int lda,
 // Causal attention of each packed prefill row against its own sequence's
 // keys in the cache (positions 0..pos).  q is [M][ldq] (head j at columns
 // j*hs), the output y [M][ldy] likewise.
+// kc / vc: this layer's cache, addressed through kv.
 void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
-                         const void* vc, const RowMap& map, int maxlen, int H,
+                         const void* vc, const KvMap& kv, const RowMap& map, int maxlen, int H,
                          int hs, int Tb, void* y, int ldy, float* part, hipStream_t s);
 // chunks per (row, head) of the prefill key split: the partial buffer holds
 // [H][Tb][chunks][hs + 4] floats (one sequence)
@@ -112,7 +142,7 @@ int attn_prefill_split_chunks(int Tb);
 int attn_decode_chunks(int Tb);
 int attn_decode_chunk_keys();
 void launch_attn_decode(int dtype, const void* q, const void* kc,
-                        const void* vc, const int32_t* pos, int B, int H,
+                        const void* vc, const KvMap& kv, const int32_t* pos, int B, int H,
                         int hs, int Tb, float* part, void* y,
                         bool merge_into_y, hipStream_t s);
 

@@ -61,6 +61,8 @@ extern "C" {
 #define NGPT_E_DEVICE    -7  /* a kernel saw invalid input (id out of range,
                                 or a logits row with no finite maximum)    */
 #define NGPT_E_TIMEOUT   -8  /* a wait in the one-launch decode kernel gave up */
+#define NGPT_E_PAGE      -9  /* a paged cache position to be written has no
+                                page mapped (reported by ngpt_device_status) */
 
 /* Element types (the fp16 model: SDK guide "极速上手nanoGPT", section
  * "性能优化技巧", mixed precision with float16). */
@@ -128,21 +130,41 @@ typedef struct {
 
 /*
  * KV cache (serving page, KV-cache section: per layer the past K and V,
- * extended by one row per new token), caller-owned device memory.  k and v
- * are each laid out [n_layer][batch][n_head][block_size][head_dim] in the
- * config dtype (ngpt_kv_bytes() bytes each).  lens[b] is the number of
- * positions of sequence b held in the cache; limit[b] (<= block_size) is
- * the total length at which sequence b stops taking tokens.  Both are
- * device int32 [batch], written by ngpt_prefill() and advanced by the decode
- * calls.  A sequence is active while lens[b] < limit[b].  k and v must be
- * 16-byte aligned.
+ * extended by one row per new token), caller-owned device memory.
+ *
+ * Contiguous (block_table == NULL): k and v are each laid out
+ * [n_layer][batch][n_head][block_size][head_dim] in the config dtype
+ * (ngpt_kv_bytes() bytes each).
+ *
+ * Paged (the paged KV memory of vLLM that the serving page's section
+ * "HF 在哪些情况下实际上会更好" names): k and v are pools of num_pages pages,
+ * each laid out [n_layer][num_pages][n_head][NGPT_PAGE_TOKENS][head_dim]
+ * (ngpt_kv_pool_bytes() bytes each).  Positions 64j .. 64j+63 of sequence b
+ * live in page block_table[b * ceil(block_size / 64) + j] (device int32
+ * [batch][ceil(block_size / 64)]); an entry outside [0, num_pages) is an
+ * unmapped block.  Sequences can share no page they both write.  The table
+ * is the caller's memory, written by the caller or with ngpt_kv_map();
+ * kernels read unmapped blocks as zeros and skip writes into them, which
+ * ngpt_device_status() reports as NGPT_E_PAGE.  The one-launch batch-1
+ * decode kernel takes contiguous caches only; a paged batch-1 cache decodes
+ * through the per-layer graph.
+ *
+ * lens[b] is the number of positions of sequence b held in the cache;
+ * limit[b] (<= block_size) is the total length at which sequence b stops
+ * taking tokens.  Both are device int32 [batch], written by ngpt_prefill()
+ * and advanced by the decode calls.  A sequence is active while lens[b] <
+ * limit[b].  k and v must be 16-byte aligned.
  */
+#define NGPT_PAGE_TOKENS 64
+
 typedef struct {
   void *k;
   void *v;
   int32_t *lens;
   int32_t *limit;
   int32_t batch;
+  int32_t num_pages;       /* pages per pool (paged), ignored otherwise */
+  int32_t *block_table;    /* NULL: contiguous layout */
 } ngpt_kv;
 
 typedef struct ngpt_model ngpt_model;
@@ -151,6 +173,11 @@ typedef struct ngpt_model ngpt_model;
  * section's per-layer K and V, block_size positions each); 0 if the config
  * is invalid or batch < 1.  Host-only, needs no GPU. */
 size_t ngpt_kv_bytes(const ngpt_config *cfg, int32_t batch);
+
+/* Bytes of ONE of the two paged KV pools of num_pages pages (each page
+ * NGPT_PAGE_TOKENS positions of every layer and head); 0 if the config is
+ * invalid or num_pages < 1.  Host-only, needs no GPU. */
+size_t ngpt_kv_pool_bytes(const ngpt_config *cfg, int32_t num_pages);
 
 /* Bytes of the workspace a model of this config needs (activations of up
  * to max(max_prefill_tokens, max_batch) rows of the forward of the SDK
@@ -289,6 +316,21 @@ int ngpt_extend(ngpt_model *m, ngpt_kv *kv, const int32_t *slots,
  * NGPT_E_RANGE, NGPT_E_HIP.
  */
 int ngpt_retire(ngpt_model *m, ngpt_kv *kv, const int32_t *slots, int32_t n);
+
+/*
+ * Map blocks first_block .. first_block + count - 1 of row `slot` of a
+ * paged cache to the pages pages[0 .. count-1] (HOST int32; -1 unmaps a
+ * block), in stream order: a later prefill, extend or decode call on the
+ * model's stream sees the new table.  This is the page bookkeeping of a
+ * paged cache (serving page, section "HF 在哪些情况下实际上会更好": vLLM's
+ * paged KV memory with continuous batching): the caller keeps the free list,
+ * maps a row's blocks before positions in them are written, and may hand a
+ * retired row's pages to another row.  Errors: NGPT_E_ARG (NULL pointers, kv
+ * not paged), NGPT_E_RANGE (slot, block range or a page id outside
+ * [-1, num_pages)), NGPT_E_HIP.
+ */
+int ngpt_kv_map(ngpt_model *m, ngpt_kv *kv, int32_t slot, int32_t first_block,
+                int32_t count, const int32_t *pages);
 
 /*
  * Generation past block_size (generate() crops its input to the last

@@ -47,6 +47,18 @@ def test_kv_bytes_matches_layout(name):
     assert ng.check_config(cfg) == ng.NGPT_OK
 
 
+def test_kv_pool_bytes_is_pages_of_64_positions():
+    # a paged pool of P pages holds P * 64 positions of every layer and head
+    w = synth.workload("gpt2_124m_bias_b64_ragged")
+    cfg = cfg_of(w)
+    assert ng.NGPT_PAGE_TOKENS == 64
+    assert ng.kv_pool_bytes(cfg, 1) == 12 * 64 * 768 * 2
+    assert ng.kv_pool_bytes(cfg, 16) == ng.kv_bytes(cfg, 1)   # 16 pages = 1024 positions
+    assert ng.kv_pool_bytes(cfg, 0) == 0
+    bad = cfg_of(w, n_head=5)
+    assert ng.kv_pool_bytes(bad, 4) == 0
+
+
 def test_kv_bytes_known_values():
     # GPT-2 124M, bf16, one sequence: 12 layers x 1024 positions x 768 x 2 B
     w = synth.workload("gpt2_124m_b1")
