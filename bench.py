@@ -210,15 +210,19 @@ def run_batched_workloads(torch, ng, synth):
     top-k 50 sampled decode until every row holds 1024 tokens), the GPT-2 XL
     shape at batch 32 (512-id prompts, 512 greedy steps), the
     Shakespeare-char shape at batch 8 (64-id prompts, 192 sampled steps),
-    and the evaluation forward with labels over one 1024-id sequence.
-    Decode is reported against HBM (bytes the steps must read) and, for the
-    large batches, MFMA (their matrix-product FLOPs); prefill against MFMA."""
+    and the evaluation forward with labels over one 1024-id sequence.  The
+    batch-64 workload runs twice: on a contiguous cache and on a paged one
+    (64-position pages in a shuffled order).  Decode is reported against HBM
+    (bytes the steps must read) and, for the large batches, MFMA (their
+    matrix-product FLOPs); prefill against MFMA."""
     res = {}
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    for name in ("gpt2_124m_bias_b64_ragged", "gpt2_xl_b32", "char_6l384_bf16_b8"):
+    runs = (("gpt2_124m_bias_b64_ragged", False), ("gpt2_124m_bias_b64_ragged", True),
+            ("gpt2_xl_b32", False), ("char_6l384_bf16_b8", False))
+    for name, paged in runs:
         w = synth.workload(name)
         W = synth.make_weights(w)
         ids, lens = synth.make_prompts(w)
@@ -229,7 +233,14 @@ def run_batched_workloads(torch, ng, synth):
             m.set_sampling(greedy=True)
         else:
             m.set_sampling(temperature=w.temperature, top_k=w.top_k)
-        kv = m.new_kv(w.batch)
+        if paged:
+            nblk = (w.block_size + 63) // 64
+            kv = m.new_kv(w.batch, num_pages=w.batch * nblk)
+            order = np.random.default_rng(w.index).permutation(w.batch * nblk)
+            for b in range(w.batch):
+                m.kv_map(kv, b, 0, order[b * nblk:(b + 1) * nblk])
+        else:
+            kv = m.new_kv(w.batch)
         nxt = torch.empty(w.batch, dtype=torch.int32, device="cuda")
         d_ids = torch.as_tensor(ids).cuda()
         t = {}
@@ -256,7 +267,7 @@ def run_batched_workloads(torch, ng, synth):
             flops += len(act) * (2 * (12 * L * C * C + V * C)) + sum(4 * L * C * (p + 1) for p in act)
         dec_s = t["decode_ms"] / 1e3
         pre_flops = prefill_flops_rows(w, [int(l) for l in lens])
-        r = {"workload": w.description,
+        r = {"workload": w.description + (", paged KV cache" if paged else ""),
              "prefill_tokens_per_s": round(float(lens.sum()) / (t["prefill_ms"] / 1e3), 1),
              "prefill_ms": round(t["prefill_ms"], 3),
              "prefill_mfma_frac": round(pre_flops / (t["prefill_ms"] / 1e3) / 1e12
@@ -266,8 +277,9 @@ def run_batched_workloads(torch, ng, synth):
              "decode_steps": steps,
              "decode_hbm_frac": round(pos_bytes / dec_s / 1e9 / HBM_PEAK_GBS, 4),
              "decode_mfma_frac": round(flops / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        res[name] = r
-        print(json.dumps({"batched": name, **r}), file=sys.stderr, flush=True)
+        key = name + ("_paged" if paged else "")
+        res[key] = r
+        print(json.dumps({"batched": key, **r}), file=sys.stderr, flush=True)
 
     # evaluation forward with labels over 1024 positions
     wp = synth.workload("gpt2_124m_prefill1024")

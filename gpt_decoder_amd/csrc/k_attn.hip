@@ -482,6 +482,146 @@ __global__ __launch_bounds__(64) void attn_decode_combine(
 }
 
 // ---------------------------------------------------------------------------
+// Decode with many (sequence, head) pairs (batched steps): one workgroup per
+// pair streams every key of its sequence and writes y itself, so the grid
+// holds no empty chunks and no merge launch follows.  Keys go in groups of
+// GK = 2 * (64 / LPK) (16 at hs 64): wavefront w takes groups w, w + 4, ...,
+// four groups in flight, each lane group keeping its own running (max, sum,
+// o[8]); lanes, then wavefronts (in order) are merged at the end.  A group
+// lies in one 64-position cache block; an unmapped block reads as zeros.
+// ---------------------------------------------------------------------------
+// One group of GK keys: the K and V rows of this lane's two passes.
+struct DecGroup {
+  uint4 k0, k1, v0, v1;
+};
+
+template <class T, int HS>
+__global__ __launch_bounds__(256) void attn_decode_rows_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    KvMap kvm, const int32_t* __restrict__ pos, int H, float scale, T* __restrict__ y) {
+  static_assert(sizeof(T) == 2, "16-bit caches only");
+  constexpr int LPK = HS / 8;          // lanes per key
+  constexpr int KPP = 64 / LPK;        // keys per wavefront pass
+  constexpr int GK = 2 * KPP;          // keys per group (two passes)
+  static_assert(kPageTokens % GK == 0, "a group must lie in one cache block");
+  __shared__ float sw[4][HS + 2];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int C = H * HS;
+  const int p = pos[b];
+  // (the wavefront index as a uniform value, so that the block-table reads
+  // are scalar loads, which do not wait behind the K/V loads in flight)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T* yo = y + (size_t)b * C + h * HS;
+  if (p < 0) {   // inactive sequence: a zero row keeps later layers finite
+    if (tid < HS) yo[tid] = from_f32<T>(0.f);
+    return;
+  }
+  const int sub = lane % LPK, kgrp = lane / LPK;
+  const int ng = p / GK + 1;                        // groups holding keys 0..p
+  const int nmine = ng > wave ? (ng - wave + 3) / 4 : 0;
+  const int64_t hoff = (int64_t)h * kv_hstride(kvm);
+  const float sl2 = scale * kLog2e;
+
+  // this wavefront's i-th group (zeros past the last one)
+  auto load = [&](int i) {
+    DecGroup g{};
+    if (i < nmine) {
+      const int g0 = (wave + 4 * i) * GK;
+      const int64_t bb = kv_block_base(kvm, b, g0 / kPageTokens);
+      if (bb >= 0) {
+        const int u0 = g0 + kgrp, u1 = g0 + KPP + kgrp;
+        const size_t o0 = (size_t)(bb + hoff + u0 % kPageTokens) * HS + sub * 8;
+        const size_t o1 = (size_t)(bb + hoff + u1 % kPageTokens) * HS + sub * 8;
+        if (u0 <= p) {
+          g.k0 = *reinterpret_cast<const uint4*>(kc + o0);
+          g.v0 = *reinterpret_cast<const uint4*>(vc + o0);
+        }
+        if (u1 <= p) {
+          g.k1 = *reinterpret_cast<const uint4*>(kc + o1);
+          g.v1 = *reinterpret_cast<const uint4*>(vc + o1);
+        }
+      }
+    }
+    return g;
+  };
+  // the query first: waiting for it then does not wait for the groups
+  const uint4 qraw = *reinterpret_cast<const uint4*>(q + (size_t)b * C + h * HS + sub * 8);
+  DecGroup g0 = load(0), g1 = load(1), g2 = load(2), g3 = load(3);
+  float qv[8];
+  Half16<T>::unpack8(qraw, qv);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qv[j] *= sl2;
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = 0.f;
+  auto pass = [&](const uint4& kraw, const uint4& vraw, int u) {
+    float kf[8];
+    Half16<T>::unpack8(kraw, kf);
+    float sc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc = fmaf(qv[j], kf[j], sc);
+#pragma unroll
+    for (int o2 = 1; o2 < LPK; o2 <<= 1) sc += __shfl_xor(sc, o2, 64);
+    if (u <= p) {
+      float vf[8];
+      Half16<T>::unpack8(vraw, vf);
+      const float mn = fmaxf(m, sc);
+      const float a = exp2_fast(m - mn);  // m = -inf gives 0
+      const float pr = exp2_fast(sc - mn);
+      l = l * a + pr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = o[j] * a + pr * vf[j];
+      m = mn;
+    }
+  };
+  auto group = [&](const DecGroup& g, int i) {
+    const int gk = (wave + 4 * i) * GK;
+    pass(g.k0, g.v0, gk + kgrp);
+    pass(g.k1, g.v1, gk + KPP + kgrp);
+  };
+  // four groups in flight: process one, then fetch the one four ahead
+  for (int i = 0; i < nmine; i += 4) {
+    group(g0, i);
+    g0 = load(i + 4);
+    if (i + 1 >= nmine) break;
+    group(g1, i + 1);
+    g1 = load(i + 5);
+    if (i + 2 >= nmine) break;
+    group(g2, i + 2);
+    g2 = load(i + 6);
+    if (i + 3 >= nmine) break;
+    group(g3, i + 3);
+    g3 = load(i + 7);
+  }
+  // merge the key slots of the wavefront (lanes differing in bits >= LPK)
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float l2 = __shfl_xor(l, off, 64);
+    float o2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o2[j] = __shfl_xor(o[j], off, 64);
+    merge_state(m, l, o, m2, l2, o2, 8);
+  }
+  if (lane < LPK) {
+    if (lane == 0) {
+      sw[wave][0] = m;
+      sw[wave][1] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sw[wave][2 + sub * 8 + j] = o[j];
+  }
+  __syncthreads();
+  if (tid < HS) {
+    float mm = -INFINITY, ll = 0.f, oo = 0.f;
+    for (int w = 0; w < 4; ++w) merge_state(mm, ll, &oo, sw[w][0], sw[w][1], &sw[w][2 + tid], 1);
+    yo[tid] = from_f32<T>(oo / ll);
+  }
+}
+
+// ---------------------------------------------------------------------------
 int attn_prefill_split_chunks(int Tb) { return ((Tb + 63) / 64 + kPrefillKch - 1) / kPrefillKch; }
 
 template <class T>
@@ -546,6 +686,10 @@ void launch_attn_prefill(int dtype, const void* q, int ldq, const void* kc,
 
 int attn_decode_chunks(int Tb) { return (Tb + kDecChunk - 1) / kDecChunk; }
 
+// (sequence, head) pairs from which a merged decode step takes one
+// workgroup per pair rather than one per 64-key chunk
+constexpr int kDecodeRowsMinPairs = 256;
+
 int attn_decode_chunk_keys() { return kDecChunk; }
 
 template <class T>
@@ -553,6 +697,17 @@ static void launch_attn_decode_t(const T* q, const T* kc, const T* vc, const KvM
                                  const int32_t* pos, int B, int H, int hs, int Tb,
                                  float* part, T* y, bool merge_into_y, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)hs);
+  if constexpr (sizeof(T) == 2) {
+    // enough (sequence, head) pairs to fill the chip: one workgroup each
+    if (merge_into_y && B * H >= kDecodeRowsMinPairs) {
+      const dim3 rgrid(H, B);
+      if (hs == 64)
+        attn_decode_rows_kernel<T, 64><<<rgrid, 256, 0, s>>>(q, kc, vc, kv, pos, H, scale, y);
+      else
+        attn_decode_rows_kernel<T, 32><<<rgrid, 256, 0, s>>>(q, kc, vc, kv, pos, H, scale, y);
+      return;
+    }
+  }
   const int nchunk = attn_decode_chunks(Tb);
   const dim3 grid(nchunk, H, B), cgrid(H, B);
   if (hs == 64) {

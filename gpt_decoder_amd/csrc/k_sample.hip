@@ -28,6 +28,7 @@
 namespace ngpt {
 
 constexpr int kSampThreads = 512;
+constexpr int kSampMaxRun = 100;   // register-resident chunks per wavefront
 
 // logit / T rounded once to fp32: the fp32 division here is IEEE
 // correctly rounded (the compiler's default division, no fast-math), so it
@@ -53,10 +54,13 @@ struct SampShared {
   float fred[kSampThreads / 64];
   int ired[kSampThreads / 64];
   double scan[1];
+  double wsum[kSampThreads / 64];
+  unsigned long long kmask[kSampThreads / 64][kSampMaxRun];   // kept lanes per chunk
   uint32_t prefix;
   uint32_t remaining;
   int found;
   int last_kept;
+  int done;
 };
 
 __device__ __forceinline__ double block_sum_d(double v, SampShared& sh) {
@@ -84,7 +88,7 @@ __device__ __forceinline__ float block_max_f(float v, SampShared& sh) {
 // Greedy: argmax of the raw logits, lowest id among equal maxima.  Each
 // thread scans its ids in ascending order, so a strict comparison keeps the
 // first of equal values.
-__device__ int row_argmax(const float* lg, int V, SampShared& sh) {
+__device__ __forceinline__ int row_argmax(const float* lg, int V, SampShared& sh) {
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
   int tail = 0;
@@ -127,13 +131,14 @@ __device__ int row_argmax(const float* lg, int V, SampShared& sh) {
 
 // Wavefront-aggregated histogram add: the lanes with `match` add 1 to
 // hist[bin]; lanes sharing a bin are counted with one atomic (logits crowd
-// into a few top-byte bins, where per-lane atomics would serialise).
+// into a few top-byte bins, where per-lane atomics would serialise).  The
+// leader's bin is read with a scalar lane read, not an LDS permute.
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool match, uint32_t bin) {
   const int lane = threadIdx.x & 63;
   unsigned long long act = __ballot(match);
   while (act) {
     const int leader = __ffsll(act) - 1;
-    const uint32_t lbin = __shfl(bin, leader, 64);
+    const uint32_t lbin = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
     const unsigned long long same = __ballot(match && bin == lbin);
     if (lane == leader) atomicAdd(&hist[lbin], (uint32_t)__popcll(same));
     act &= ~same;
@@ -157,7 +162,7 @@ __device__ __forceinline__ double block_scan_incl(double v, SampShared& sh) {
   return before + v;
 }
 
-__device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
+__device__ __forceinline__ int row_sample(const float* lg, int V, float T, int top_k, double u,
                           SampShared& sh) {
   const int tid = threadIdx.x;
   // -- threshold: the k'-th largest scaled logit, k' = min(top_k, V)
@@ -170,10 +175,19 @@ __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
       for (int i = tid; i < 256; i += kSampThreads) sh.hist[i] = 0;
       __syncthreads();
       const uint32_t prefix = sh.prefix;
-      for (int i0 = 0; i0 < V; i0 += kSampThreads) {   // uniform trip count
-        const int i = i0 + tid;
-        const uint32_t k = i < V ? fkey(scaled(lg[i], T)) : 0u;
-        hist_add(sh.hist, i < V && (k & mask) == prefix, (k >> shift) & 0xFFu);
+      constexpr int U = 4;   // loads issued before their histogram adds
+      for (int i0 = 0; i0 < V; i0 += U * kSampThreads) {   // uniform trip count
+        uint32_t k[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kSampThreads + tid;
+          k[u] = i < V ? fkey(scaled(lg[i], T)) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kSampThreads + tid;
+          hist_add(sh.hist, i < V && (k[u] & mask) == prefix, (k[u] >> shift) & 0xFFu);
+        }
       }
       __syncthreads();
       if (tid == 0) {
@@ -235,6 +249,140 @@ __device__ int row_sample(const float* lg, int V, float T, int top_k, double u,
   return sh.found != 0x7FFFFFFF ? sh.found : sh.last_kept;
 }
 
+// Sum over the wavefront, the same value in every lane (each butterfly
+// step adds a pair in both orders, which IEEE addition rounds alike).
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// The draw with the row's scaled logits held in registers as order keys,
+// read and divided once for the threshold and the maximum.  Wavefront w
+// owns ids [64 RUN w, 64 RUN (w + 1)) as RUN chunks of 64 consecutive ids,
+// lane l holding id 64 RUN w + 64 j + l of chunk j (coalesced loads).
+// Requires V <= 512 RUN.  Each chunk's kept lanes go to LDS as a mask; the
+// weights are then formed for kept ids only, re-reading their logits (the
+// same division gives the same value), in a plain loop over the chunks.
+// Running sums go chunk by chunk: a chunk's kept weights are summed over the
+// wavefront, the wavefront totals in wavefront order, and the chunk holding
+// u * S is scanned lane by lane; chunks without a kept id are skipped.
+template <int RUN>
+__device__ __forceinline__ int row_sample_regs(const float* lg, int V, float T, int top_k, double u,
+                               SampShared& sh) {
+  static_assert(RUN <= kSampMaxRun, "chunk masks are sized for kSampMaxRun");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int base = wave * 64 * RUN;
+  uint32_t key[RUN];
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    const int i = base + 64 * j + lane;
+    key[j] = i < V ? fkey(scaled(lg[i], T)) : 0u;
+  }
+  auto valid = [&](int j) { return base + 64 * j + lane < V; };
+
+  // -- threshold key: the k'-th largest, k' = min(top_k, V); 0 keeps all
+  uint32_t thr = 0;
+  if (top_k > 0 && top_k < V) {
+    if (tid == 0) { sh.prefix = 0; sh.remaining = (uint32_t)top_k; sh.done = 0; }
+    uint32_t mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      __syncthreads();
+      for (int i = tid; i < 256; i += kSampThreads) sh.hist[i] = 0;
+      __syncthreads();
+      const uint32_t prefix = sh.prefix;
+#pragma unroll
+      for (int j = 0; j < RUN; ++j)
+        if (valid(j) && (key[j] & mask) == prefix) atomicAdd(&sh.hist[(key[j] >> shift) & 0xFFu], 1u);
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t rem = sh.remaining, cum = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (cum + sh.hist[d] >= rem) break;
+          cum += sh.hist[d];
+        }
+        sh.remaining = rem - cum;
+        sh.prefix = prefix | ((uint32_t)d << shift);
+        // the bin holds exactly the ids still wanted: every key at or above
+        // the bin's lowest possible key is kept, so the search can stop
+        sh.done = cum + sh.hist[d] == rem;
+      }
+      __syncthreads();
+      mask |= 0xFFu << shift;
+      if (sh.done) break;
+    }
+    thr = sh.prefix;
+  }
+
+  // -- kept masks and the max of the kept values (the overall max is kept)
+  // (lane l collects the masks of chunks l and l + 64, then stores them)
+  float lmax = -INFINITY;
+  unsigned long long my0 = 0, my1 = 0;
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) {
+    const unsigned long long km = __ballot(valid(j) && key[j] >= thr);
+    if (j < 64) my0 = lane == j ? km : my0;
+    else my1 = lane == j - 64 ? km : my1;
+    if (valid(j)) lmax = fmaxf(lmax, key_to_float(key[j]));
+  }
+  if (lane < RUN) sh.kmask[wave][lane] = my0;
+  if (lane + 64 < RUN) sh.kmask[wave][lane + 64] = my1;
+  const double m = (double)block_max_f(lmax, sh);   // (its barrier publishes the masks)
+
+  // -- this wavefront's total, chunk by chunk, and its last kept id
+  auto weight = [&](int j, unsigned long long km) {
+    return ((km >> lane) & 1) ? exp((double)scaled(lg[base + 64 * j + lane], T) - m) : 0.0;
+  };
+  double wt = 0.0;
+  int lk = -1;
+  for (int j = 0; j < RUN; ++j) {
+    const unsigned long long km = sh.kmask[wave][j];
+    if (km == 0) continue;
+    wt += wave_sum_d(weight(j, km));
+    lk = base + 64 * j + 63 - __clzll(km);
+  }
+  if (lane == 0) sh.wsum[wave] = wt;
+  if (tid == 0) { sh.found = 0x7FFFFFFF; sh.last_kept = -1; }
+  __syncthreads();
+  if (lane == 0 && lk >= 0) atomicMax(&sh.last_kept, lk);
+  double S = 0.0, C = 0.0;
+  for (int w = 0; w < kSampThreads / 64; ++w) {
+    if (w == wave) C = S;
+    S += sh.wsum[w];
+  }
+  const double target = u * S;
+  if (C <= target && C + wt > target) {   // the wavefront holding the draw
+    double c = C;
+    int hit = -1;
+    for (int j = 0; j < RUN; ++j) {
+      const unsigned long long km = sh.kmask[wave][j];
+      if (km == 0) continue;
+      const double w = weight(j, km);
+      const double cs = wave_sum_d(w);
+      if (c + cs > target) {
+        // running sum over the lanes of this chunk, ascending ids
+        double incl = w;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        const unsigned long long over = __ballot(((km >> lane) & 1) && c + incl > target);
+        // rounding may leave no lane above u * S: the chunk's last kept id
+        const int l = over ? __ffsll(over) - 1 : 63 - __clzll(km);
+        hit = base + 64 * j + l;
+        break;
+      }
+      c += cs;
+    }
+    if (lane == 0) sh.found = hit >= 0 ? hit : 0x7FFFFFFF;
+  }
+  __syncthreads();
+  return sh.found != 0x7FFFFFFF ? sh.found : sh.last_kept;
+}
+
 template <class T>
 __device__ void write_embedding(const T* wte, const T* wpe, int id, int p,
                                 int C, float* xr) {
@@ -289,7 +437,14 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
         id = 0;
       }
     } else {
-      id = row_sample(lg, V, p.temperature, p.top_k, uniforms[b], sh);
+      const int run = (V + kSampThreads - 1) / kSampThreads;
+      const double u = uniforms[b];
+      if (run <= 1) id = row_sample_regs<1>(lg, V, p.temperature, p.top_k, u, sh);
+      else if (run <= 4) id = row_sample_regs<4>(lg, V, p.temperature, p.top_k, u, sh);
+      else if (run <= 16) id = row_sample_regs<16>(lg, V, p.temperature, p.top_k, u, sh);
+      else if (run <= 40) id = row_sample_regs<40>(lg, V, p.temperature, p.top_k, u, sh);
+      else if (run <= 100) id = row_sample_regs<100>(lg, V, p.temperature, p.top_k, u, sh);
+      else id = row_sample(lg, V, p.temperature, p.top_k, u, sh);
     }
   }
   if (threadIdx.x == 0) {

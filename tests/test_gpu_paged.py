@@ -263,3 +263,47 @@ def test_unmapped_block_is_reported_not_written():
             fn()
         assert ei.value.code == code
     m.close()
+
+
+def test_paged_batch64_matches_contiguous_bitwise():
+    """64 rows x 4 heads, enough (sequence, head) pairs for the decode
+    attention that gives each pair one workgroup, and 64-row linear layers:
+    ragged prompts of 1..200 ids, then 40 teacher-forced steps.  The paged
+    cache (pages in a shuffled order) gives the contiguous cache's logits
+    bit for bit, and every row follows the oracle."""
+    torch = need_gpu()
+    w = small("bf16", batch=64, Tb=256)
+    W = synth.make_weights(w, gamma_std=0.1)
+    rng = np.random.default_rng(16)
+    lens = rng.integers(1, 201, 64)
+    toks = rng.integers(0, w.vocab_size, (64, 200)).astype(np.int32)
+    feeds = rng.integers(0, w.vocab_size, (40, 64)).astype(np.int32)
+    m = make_model(w, W, max_batch=64, max_prefill_tokens=int(lens.sum()))
+
+    def run(paged):
+        kv = m.new_kv(64, num_pages=256 if paged else None)
+        if paged:
+            order = np.random.default_rng(6).permutation(256)
+            for b in range(64):
+                m.kv_map(kv, b, 0, order[4 * b:4 * b + 4])
+        m.prefill(kv, toks, list(lens))
+        outs = [m.logits(64).cpu().numpy()]
+        for s in range(40):
+            m.decode_feed(kv, dev_i32(feeds[s]))
+            outs.append(m.logits(64).cpu().numpy())
+        assert m.device_status() == 0
+        assert kv.lens.cpu().tolist() == [int(x) + 40 for x in lens]
+        return outs
+
+    ref = run(False)
+    got = run(True)
+    diffs = [int(np.sum(a.view(np.uint32) != b.view(np.uint32))) for a, b in zip(ref, got)]
+    o = make_oracle(w, W)
+    errs = [max_abs(got[0], o.prefill(toks, list(lens)))]
+    for s in range(40):
+        errs.append(max_abs(got[1 + s], o.decode(feeds[s])))
+    log(f"  batch 64 paged vs contiguous differing logits per call max {max(diffs)}; "
+        f"oracle max err {max(errs):.2e}")
+    assert max(diffs) == 0
+    assert max(errs) < TOL_BF16
+    m.close()
