@@ -127,6 +127,19 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
     const int c = j * 256 + lane * 4;
     v[j] = c < C ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // gain and shift fetched with the row, so that one memory latency is
+  // exposed rather than two
+  float wv[kLnMaxVec][4], bv[kLnMaxVec][4];
+#pragma unroll
+  for (int j = 0; j < kLnMaxVec; ++j) {
+    const int c = j * 256 + lane * 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wv[j][u] = bv[j][u] = 0.f;
+    if (c < C) {
+      load4(w + c, wv[j]);
+      if (bias) load4(bias + c, bv[j]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
   const float mean = wave_sum(s) / (float)C;
@@ -146,13 +159,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
     const int c = j * 256 + lane * 4;
     if (c < C) {
       const float xv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-      float wv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
-      load4(w + c, wv);
-      if (bias) load4(bias + c, bv);
+      float y[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        y[u] = (xv[u] - mean) * rstd * wv[u];
-        if (bias) y[u] += bv[u];
+        y[u] = (xv[u] - mean) * rstd * wv[j][u];
+        if (bias) y[u] += bv[j][u];
       }
       store4(o + c, y);
     }

@@ -11,57 +11,21 @@
 //
 // Kernels:
 //   gemm_mfma_kernel  bf16 MFMA (v_mfma_f32_16x16x32_bf16) tile GEMM for
-//                     many rows (prefill, batched decode);
+//                     many rows (prefill, eval);
 //   gemv_kernel       streaming matrix-vector kernel for up to 4 rows (decode),
 //                     bandwidth-bound: 16-byte weight loads issued ahead of the
 //                     activations, optional fused LayerNorm prologue;
 //   gemm_f32_kernel   fp32 tiled kernel (the fp32 model).
+// (5 to 64 rows of a batched decode step go to the skinny kernel of
+// k_skinny.hip.)
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "kernels.hpp"
 
 namespace ngpt {
 
 constexpr int kGemvMaxRows = 4;  // rows handled by the streaming kernels
 constexpr int kGemvLnMaxK = 2048;  // widest row the fused LayerNorm holds (n_embd limit)
-
-template <class T, int EPI>
-__device__ __forceinline__ void epi_apply(const EpiArgs& e, int r, int n,
-                                          float acc) {
-  if constexpr (EPI == EPI_LOGITS) {
-    if (e.row_pos && e.row_pos[r] < 0) return;
-    const int orow = e.row_b ? e.row_b[r] : r;   // the sequence's logits row
-    static_cast<float*>(e.out)[(size_t)orow * e.ldo + n] = acc;
-    return;
-  } else {
-    float v = acc;
-    if (e.bias) v += to_f32(static_cast<const T*>(e.bias)[n]);
-    if constexpr (EPI == EPI_GELU) {
-      static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(gelu_erf(v));
-    } else if constexpr (EPI == EPI_RESID) {
-      static_cast<float*>(e.out)[(size_t)r * e.ldo + n] += v;
-    } else if constexpr (EPI == EPI_QKV) {
-      const int which = n / e.C;
-      const int c = n - which * e.C;
-      if (which == 0) {
-        static_cast<T*>(e.out)[(size_t)r * e.ldo + c] = from_f32<T>(v);
-        return;
-      }
-      const int p = e.row_pos[r];
-      if (p < 0) return;
-      const int b = e.row_b ? e.row_b[r] : r;
-      const int64_t base = kv_block_base(e.kv, b, p / kPageTokens);
-      if (base < 0) {   // unmapped block of a paged cache
-        if (e.status) atomicOr(e.status, 4);
-        return;
-      }
-      const int h = c / e.hs;
-      const int d = c - h * e.hs;
-      T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
-      cache[(size_t)(base + (int64_t)h * kv_hstride(e.kv) + p % kPageTokens) * e.hs + d] =
-          from_f32<T>(v);
-    }
-  }
-}
 
 // A 16-bit element from its bit pattern.
 template <class T> __device__ __forceinline__ float bits_to_f32(uint32_t u16);
@@ -394,101 +358,6 @@ __device__ __forceinline__ void load_vec(const float* p, float* f) {
   const float4 t = *reinterpret_cast<const float4*>(p);
   f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
 }
-// ---------------------------------------------------------------------------
-// Skinny 16-bit MFMA GEMM for a few rows (M <= 64: the rows of a batched
-// decode step), where a tile GEMM has too few tiles to keep the chip busy
-// and its K loop waits on LDS and barriers.  A workgroup owns a strip of
-// 16 * NT output columns and all M rows (16 * MT, zero-padded); its four
-// wavefronts take the K steps of 32 in turn (wavefront w: steps w, w + 4,
-// ...), each loading both MFMA operands straight from global memory into
-// registers, D steps ahead, with no LDS and no barrier in the loop.  NI is
-// the most steps a wavefront takes; steps past K / 32 read zeros.  The
-// four partial sums meet in LDS and are added in wavefront order, then the
-// epilogue runs per element.  The operand layout is the tile GEMM's (A
-// fragment first): lane l feeds row l % 16 of A and column l % 16 of W with
-// the same 8 consecutive K values 8 * (l / 16) of the step; element i of the
-// 16x16 result is row 4 * (l / 16) + i, column l % 16.
-// ---------------------------------------------------------------------------
-constexpr int kSkinnyMaxRows = 64;
-
-template <class T, int EPI, int MT, int NT, int NI>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
-    const T* __restrict__ A, int lda, const T* __restrict__ W, int M, int N, int K,
-    EpiArgs e) {
-  typedef typename Half16<T>::vec8 vec8;
-  constexpr int D = NI < 8 ? NI : 8;   // steps in flight per wavefront
-  constexpr uint32_t kOut = 0x80000000u;
-  constexpr int BN = 16 * NT, BM = 16 * MT;
-  __shared__ float red[4][BM][BN + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * BN;
-  const int g = lane >> 4;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(A), (short)0, (int)((uint32_t)M * (uint32_t)lda * 2u), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * 2u), 0x00020000);
-  uint32_t aoff[MT], woff[NT];   // byte offsets at K = 0 (kOut: zero rows)
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int r = 16 * i + (lane & 15);
-    aoff[i] = r < M ? ((uint32_t)r * (uint32_t)lda + 8u * g) * 2u : kOut;
-  }
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int n = n0 + 16 * j + (lane & 15);
-    woff[j] = n < N ? ((uint32_t)n * (uint32_t)K + 8u * g) * 2u : kOut;
-  }
-  vec8 fa[D][MT], fw[D][NT];
-  const int nsteps = K / 32;
-  auto load = [&](int st, int i) {
-    const int step = wave + 4 * i;
-    const bool in = step < nsteps;
-    const uint32_t kb = (uint32_t)(32 * step) * 2u;   // this step's K, bytes
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-      fa[st][m] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-          ra, (aoff[m] == kOut || !in) ? kOut : aoff[m] + kb, 0, 0));
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      fw[st][j] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-          rw, (woff[j] == kOut || !in) ? kOut : woff[j] + kb, 0, 0));
-  };
-  f32x4_t acc[MT][NT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // (scheduling barriers keep the compiler from sinking the loads towards
-  // their use, which would leave fewer steps in flight)
-#pragma unroll
-  for (int i = 0; i < D; ++i) load(i, i);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int st = i % D;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[m][j] = Half16<T>::mfma(fa[st][m], fw[st][j], acc[m][j]);
-    if (i + D < NI) load(st, i + D);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][16 * m + 4 * g + v][16 * j + (lane & 15)] = acc[m][j][v];
-  __syncthreads();
-  for (int idx = tid; idx < BM * BN; idx += 256) {
-    const int r = idx / BN, c = idx % BN;
-    const int n = n0 + c;
-    if (r >= M || n >= N) continue;
-    const float v = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
-    epi_apply<T, EPI>(e, r, n, v);
-  }
-}
-
 template <class T>
 __device__ __forceinline__ float round_to(float v) {
   return to_f32(from_f32<T>(v));
@@ -909,34 +778,6 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   }
 }
 
-// Skinny GEMM for 4 < M <= 64 (K a multiple of 32): steps per wavefront
-// bucketed for the GPT-2 widths, K <= 768 (6), <= 1664 (13: n_embd 1600),
-// and for the MLP projection K <= 3072 (24) and <= 6400 (50); false when the
-// shape is not covered.
-template <class T, int EPI>
-static bool dispatch_skinny(const T* a, int lda, const T* w, int M, int N, int K,
-                            const EpiArgs& e, hipStream_t s) {
-  if (M > kSkinnyMaxRows || K % 32 != 0) return false;
-  constexpr int NT = EPI == EPI_LOGITS ? 2 : 1;
-  const int grid = (N + 16 * NT - 1) / (16 * NT);
-  const bool m2 = M <= 32;
-  const int ni = (K / 32 + 3) / 4;
-#define NGPT_SKINNY(NI)                                                                    \
-  do {                                                                                     \
-    if (m2) gemm_skinny_kernel<T, EPI, 2, NT, NI><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e); \
-    else gemm_skinny_kernel<T, EPI, 4, NT, NI><<<grid, 256, 0, s>>>(a, lda, w, M, N, K, e);    \
-    return true;                                                                           \
-  } while (0)
-  if (ni <= 6) NGPT_SKINNY(6);
-  if (ni <= 13) NGPT_SKINNY(13);
-  if constexpr (EPI == EPI_RESID) {
-    if (ni <= 24) NGPT_SKINNY(24);
-    if (ni <= 50) NGPT_SKINNY(50);
-  }
-#undef NGPT_SKINNY
-  return false;
-}
-
 template <class T, int EPI>
 static void dispatch_gemv(const void* A, int lda, const LnArgs* ln, const void* W,
                           int M, int N, int K, const EpiArgs& e, hipStream_t s) {
@@ -969,12 +810,12 @@ static void dispatch(int dtype, const void* A, int lda, const LnArgs* ln,
   if (dtype == NGPT_BF16) {
     const bf16_t* a = static_cast<const bf16_t*>(A);
     const bf16_t* w = static_cast<const bf16_t*>(W);
-    if (!dispatch_skinny<bf16_t, EPI>(a, lda, w, M, N, K, e, s))
+    if (!launch_skinny(NGPT_BF16, EPI, a, lda, w, M, N, K, e, s))
       dispatch_mfma<bf16_t, EPI>(a, lda, w, M, N, K, e, s);
   } else if (dtype == NGPT_F16) {
     const f16_t* a = static_cast<const f16_t*>(A);
     const f16_t* w = static_cast<const f16_t*>(W);
-    if (!dispatch_skinny<f16_t, EPI>(a, lda, w, M, N, K, e, s))
+    if (!launch_skinny(NGPT_F16, EPI, a, lda, w, M, N, K, e, s))
       dispatch_mfma<f16_t, EPI>(a, lda, w, M, N, K, e, s);
   } else {
     const dim3 grid((N + 15) / 16, (M + 15) / 16);

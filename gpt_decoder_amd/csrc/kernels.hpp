@@ -123,6 +123,11 @@ void launch_linear(int dtype, int epi, const void* A, int lda,
                    const LnArgs* ln, const void* W, int M, int N, int K,
                    const EpiArgs& e, hipStream_t s);
 
+// Skinny 16-bit linear layer for 1 <= M <= 64 rows (K a multiple of 32 and
+// at most 13 * 16 steps of 32); false (nothing launched) for other shapes.
+bool launch_skinny(int dtype, int epi, const void* A, int lda, const void* W, int M, int N,
+                   int K, const EpiArgs& e, hipStream_t s);
+
 // Causal attention of each packed prefill row against its own sequence's
 // keys in the cache (positions 0..pos).  q is [M][ldq] (head j at columns
 // j*hs), the output y [M][ldy] likewise.
