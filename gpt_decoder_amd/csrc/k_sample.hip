@@ -14,12 +14,13 @@
 //         or the largest id in K if rounding leaves none.
 // Greedy mode is the argmax of the logits with the lowest id among ties.
 //
-// One 512-thread workgroup per row.  The k-th largest value is found by a
+// One 1024-thread workgroup per row.  The k-th largest value is found by a
 // radix select over order-preserving 32-bit keys, most significant byte
-// first, with the histogram adds aggregated per wavefront.  The running sum
-// is a two-level scan: each thread owns a contiguous run of ids, the
-// per-thread totals are prefix-summed across the workgroup, then the owning
-// thread walks its run.
+// first.  Rows of up to 1024 * 50 ids keep their keys in registers
+// (row_sample_regs: the first digit from counts below the row maximum, the
+// running sum chunk by chunk); longer rows stream from memory (row_sample:
+// each thread owns a contiguous run of ids, the per-thread totals are
+// prefix-summed across the workgroup, then the owning thread walks its run).
 #include <math.h>
 
 #include "common.hpp"
@@ -27,8 +28,8 @@
 
 namespace ngpt {
 
-constexpr int kSampThreads = 512;
-constexpr int kSampMaxRun = 100;   // register-resident chunks per wavefront
+constexpr int kSampThreads = 1024;
+constexpr int kSampMaxRun = 50;    // register-resident chunks per wavefront
 
 // logit / T rounded once to fp32: the fp32 division here is IEEE
 // correctly rounded (the compiler's default division, no fast-math), so it
@@ -56,6 +57,7 @@ struct SampShared {
   double scan[1];
   double wsum[kSampThreads / 64];
   unsigned long long kmask[kSampThreads / 64][kSampMaxRun];   // kept lanes per chunk
+  float wcnt[kSampThreads / 64][4];   // per-wavefront counts of the top digits
   uint32_t prefix;
   uint32_t remaining;
   int found;
@@ -162,6 +164,54 @@ __device__ __forceinline__ double block_scan_incl(double v, SampShared& sh) {
   return before + v;
 }
 
+// One radix level of the top-k threshold search, after the histogram of
+// the level's digit (over the keys matching the prefix so far) is in
+// sh.hist: the digit d is the highest bin where the count of keys in bins
+// >= d reaches the number still wanted, S(d) >= rem with S the suffix sums;
+// the keys in bins above d are kept, and rem - S(d + 1) are still wanted
+// from bin d.  Wavefront 0 does it: lane l holds bins 4l .. 4l + 3, the
+// suffix sums run over the lanes from the top, and d is the largest bin with
+// S(d) >= rem (S never grows with d).  Sets sh.prefix, sh.remaining and
+// sh.done (the bin holds exactly the keys still wanted).  Integer sums:
+// exact, so the same digit as a serial walk from the top.
+__device__ __forceinline__ void radix_pick(SampShared& sh, uint32_t prefix, int shift) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const uint32_t rem = sh.remaining;
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = sh.hist[4 * lane + i];
+  const uint32_t ls = (h[0] + h[1]) + (h[2] + h[3]);
+  uint32_t t = ls;   // sum over lanes >= this one
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_down(t, o, 64);
+    if (lane + o < 64) t += u;
+  }
+  // suffix sums of this lane's bins, from its top bin down
+  uint32_t sfx[4];
+  sfx[3] = t - ls + h[3];
+  sfx[2] = sfx[3] + h[2];
+  sfx[1] = sfx[2] + h[1];
+  sfx[0] = sfx[1] + h[0];
+  int best = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (sfx[i] >= rem) best = 4 * lane + i;
+  int d = best;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) d = max(d, __shfl_xor(d, o, 64));
+  // (bin 0 always qualifies: the keys matching the prefix number >= rem)
+  if (d < 0) d = 0;
+  if (lane == d / 4) {
+    const int i = d % 4;
+    const uint32_t above = sfx[i] - h[i];
+    sh.remaining = rem - above;
+    sh.prefix = prefix | ((uint32_t)d << shift);
+    sh.done = sfx[i] == rem;
+  }
+}
+
 __device__ __forceinline__ int row_sample(const float* lg, int V, float T, int top_k, double u,
                           SampShared& sh) {
   const int tid = threadIdx.x;
@@ -190,16 +240,7 @@ __device__ __forceinline__ int row_sample(const float* lg, int V, float T, int t
         }
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t rem = sh.remaining, cum = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (cum + sh.hist[d] >= rem) break;
-          cum += sh.hist[d];
-        }
-        sh.remaining = rem - cum;
-        sh.prefix = prefix | ((uint32_t)d << shift);
-      }
+      radix_pick(sh, prefix, shift);
       mask |= 0xFFu << shift;
     }
     __syncthreads();
@@ -249,11 +290,23 @@ __device__ __forceinline__ int row_sample(const float* lg, int V, float T, int t
   return sh.found != 0x7FFFFFFF ? sh.found : sh.last_kept;
 }
 
-// Sum over the wavefront, the same value in every lane (each butterfly
-// step adds a pair in both orders, which IEEE addition rounds alike).
+// Sum of a double over the wavefront with the DPP and permlane moves of
+// common.hpp applied to both 32-bit halves (no LDS permutes): every lane
+// gets the same bits, as each step adds a symmetric pair of partial sums.
+template <class F>
+__device__ __forceinline__ double move_d(double v, F mov) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __float_as_uint(mov(__uint_as_float((uint32_t)u)));
+  const uint32_t hi = __float_as_uint(mov(__uint_as_float((uint32_t)(u >> 32))));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  v += move_d(v, lane_xor1);
+  v += move_d(v, lane_xor2);
+  v += move_d(v, lane_mirror8);
+  v += move_d(v, lane_xor8);
+  v += move_d(v, lane_xor16);
+  v += move_d(v, lane_xor32);
   return v;
 }
 
@@ -261,7 +314,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // read and divided once for the threshold and the maximum.  Wavefront w
 // owns ids [64 RUN w, 64 RUN (w + 1)) as RUN chunks of 64 consecutive ids,
 // lane l holding id 64 RUN w + 64 j + l of chunk j (coalesced loads).
-// Requires V <= 512 RUN.  Each chunk's kept lanes go to LDS as a mask; the
+// Requires V <= 1024 RUN.  Each chunk's kept lanes go to LDS as a mask; the
 // weights are then formed for kept ids only, re-reading their logits (the
 // same division gives the same value), in a plain loop over the chunks.
 // Running sums go chunk by chunk: a chunk's kept weights are summed over the
@@ -274,20 +327,79 @@ __device__ __forceinline__ int row_sample_regs(const float* lg, int V, float T, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int base = wave * 64 * RUN;
+  // Range-checked buffer loads (an id past V reads 0): every load is issued
+  // on every path, all before the first use, where loads under a per-lane
+  // branch would each be waited for in turn.
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(lg), (short)0, V * 4, 0x00020000);
+  auto ld = [&](int i, bool on) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        rl, on ? (uint32_t)i * 4u : kOut, 0, 0));
+  };
   uint32_t key[RUN];
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
     const int i = base + 64 * j + lane;
-    key[j] = i < V ? fkey(scaled(lg[i], T)) : 0u;
+    key[j] = __float_as_uint(ld(i, i < V));
   }
   auto valid = [&](int j) { return base + 64 * j + lane < V; };
+#pragma unroll
+  for (int j = 0; j < RUN; ++j)
+    key[j] = valid(j) ? fkey(scaled(__uint_as_float(key[j]), T)) : 0u;
+
+  // -- the maximum (it is always kept, and it bounds the threshold's top digit)
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < RUN; ++j)
+    if (valid(j)) lmax = fmaxf(lmax, key_to_float(key[j]));
+  const float mx = block_max_f(lmax, sh);
+  const double m = (double)mx;
 
   // -- threshold key: the k'-th largest, k' = min(top_k, V); 0 keeps all
   uint32_t thr = 0;
   if (top_k > 0 && top_k < V) {
     if (tid == 0) { sh.prefix = 0; sh.remaining = (uint32_t)top_k; sh.done = 0; }
-    uint32_t mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    // First digit from counts of the four top digits at and below the
+    // maximum's, kept in registers (the logits crowd into a few top-byte
+    // bins, where histogram atomics would collide); the histogram pass runs
+    // only if the k'-th largest lies lower.
+    const int mb = (int)(fkey(mx) >> 24);
+    float c[4] = {0.f, 0.f, 0.f, 0.f};   // counts below 2^24: exact
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      const int d = (int)(key[j] >> 24);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += (valid(j) && d == mb - i) ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = wave_sum_all(c[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.wcnt[wave][i] = c[i];
+    }
+    __syncthreads();
+    int shift0 = 24;
+    {
+      uint32_t cum = 0;
+      for (int i = 0; i < 4 && mb - i >= 0; ++i) {
+        uint32_t ci = 0;
+        for (int w = 0; w < kSampThreads / 64; ++w) ci += (uint32_t)sh.wcnt[w][i];
+        if (cum + ci >= (uint32_t)top_k) {   // the k'-th largest has digit mb - i
+          shift0 = 16;
+          if (tid == 0) {
+            sh.prefix = (uint32_t)(mb - i) << 24;
+            sh.remaining = (uint32_t)top_k - cum;
+            sh.done = cum + ci == (uint32_t)top_k;
+          }
+          break;
+        }
+        cum += ci;
+      }
+    }
+    __syncthreads();
+    uint32_t mask = shift0 == 24 ? 0u : 0xFF000000u;
+    for (int shift = shift0; shift >= 0 && !sh.done; shift -= 8) {
       __syncthreads();
       for (int i = tid; i < 256; i += kSampThreads) sh.hist[i] = 0;
       __syncthreads();
@@ -296,19 +408,9 @@ __device__ __forceinline__ int row_sample_regs(const float* lg, int V, float T, 
       for (int j = 0; j < RUN; ++j)
         if (valid(j) && (key[j] & mask) == prefix) atomicAdd(&sh.hist[(key[j] >> shift) & 0xFFu], 1u);
       __syncthreads();
-      if (tid == 0) {
-        uint32_t rem = sh.remaining, cum = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (cum + sh.hist[d] >= rem) break;
-          cum += sh.hist[d];
-        }
-        sh.remaining = rem - cum;
-        sh.prefix = prefix | ((uint32_t)d << shift);
-        // the bin holds exactly the ids still wanted: every key at or above
-        // the bin's lowest possible key is kept, so the search can stop
-        sh.done = cum + sh.hist[d] == rem;
-      }
+      // (done: the bin holds exactly the ids still wanted, so every key at
+      // or above the bin's lowest possible key is kept and the search stops)
+      radix_pick(sh, prefix, shift);
       __syncthreads();
       mask |= 0xFFu << shift;
       if (sh.done) break;
@@ -316,32 +418,52 @@ __device__ __forceinline__ int row_sample_regs(const float* lg, int V, float T, 
     thr = sh.prefix;
   }
 
-  // -- kept masks and the max of the kept values (the overall max is kept)
-  // (lane l collects the masks of chunks l and l + 64, then stores them)
-  float lmax = -INFINITY;
+  // -- kept masks (lane l collects the masks of chunks l and l + 64, then
+  // stores them)
   unsigned long long my0 = 0, my1 = 0;
 #pragma unroll
   for (int j = 0; j < RUN; ++j) {
     const unsigned long long km = __ballot(valid(j) && key[j] >= thr);
     if (j < 64) my0 = lane == j ? km : my0;
     else my1 = lane == j - 64 ? km : my1;
-    if (valid(j)) lmax = fmaxf(lmax, key_to_float(key[j]));
   }
   if (lane < RUN) sh.kmask[wave][lane] = my0;
   if (lane + 64 < RUN) sh.kmask[wave][lane + 64] = my1;
-  const double m = (double)block_max_f(lmax, sh);   // (its barrier publishes the masks)
+  __syncthreads();
 
-  // -- this wavefront's total, chunk by chunk, and its last kept id
-  auto weight = [&](int j, unsigned long long km) {
-    return ((km >> lane) & 1) ? exp((double)scaled(lg[base + 64 * j + lane], T) - m) : 0.0;
+  // -- this wavefront's total, chunk by chunk, and its last kept id; the
+  // kept logits of 8 chunks are fetched together (one memory latency per 8
+  // chunks rather than per chunk)
+  constexpr int CB = 8;
+  unsigned long long km[CB];
+  float lv[CB];
+  // (returns whether any of the 8 chunks has a kept id; none: nothing fetched)
+  auto fetch = [&](int j0) {
+    unsigned long long any = 0;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      km[u] = j0 + u < RUN ? sh.kmask[wave][j0 + u] : 0ull;
+      any |= km[u];
+    }
+    if (any == 0) return false;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      lv[u] = ld(base + 64 * (j0 + u) + lane, (km[u] >> lane) & 1);
+    return true;
+  };
+  auto weight = [&](int u) {
+    return ((km[u] >> lane) & 1) ? exp((double)scaled(lv[u], T) - m) : 0.0;
   };
   double wt = 0.0;
   int lk = -1;
-  for (int j = 0; j < RUN; ++j) {
-    const unsigned long long km = sh.kmask[wave][j];
-    if (km == 0) continue;
-    wt += wave_sum_d(weight(j, km));
-    lk = base + 64 * j + 63 - __clzll(km);
+  for (int j0 = 0; j0 < RUN; j0 += CB) {
+    if (!fetch(j0)) continue;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (km[u] == 0) continue;
+      wt += wave_sum_d(weight(u));
+      lk = base + 64 * (j0 + u) + 63 - __clzll(km[u]);
+    }
   }
   if (lane == 0) sh.wsum[wave] = wt;
   if (tid == 0) { sh.found = 0x7FFFFFFF; sh.last_kept = -1; }
@@ -356,26 +478,29 @@ __device__ __forceinline__ int row_sample_regs(const float* lg, int V, float T, 
   if (C <= target && C + wt > target) {   // the wavefront holding the draw
     double c = C;
     int hit = -1;
-    for (int j = 0; j < RUN; ++j) {
-      const unsigned long long km = sh.kmask[wave][j];
-      if (km == 0) continue;
-      const double w = weight(j, km);
-      const double cs = wave_sum_d(w);
-      if (c + cs > target) {
-        // running sum over the lanes of this chunk, ascending ids
-        double incl = w;
+    for (int j0 = 0; j0 < RUN && hit < 0; j0 += CB) {
+      if (!fetch(j0)) continue;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const double t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
+      for (int u = 0; u < CB; ++u) {
+        if (km[u] == 0 || hit >= 0) continue;
+        const double w = weight(u);
+        const double cs = wave_sum_d(w);
+        if (c + cs > target) {
+          // running sum over the lanes of this chunk, ascending ids
+          double incl = w;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const double t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+          }
+          const unsigned long long over = __ballot(((km[u] >> lane) & 1) && c + incl > target);
+          // rounding may leave no lane above u * S: the chunk's last kept id
+          const int l = over ? __ffsll(over) - 1 : 63 - __clzll(km[u]);
+          hit = base + 64 * (j0 + u) + l;
+        } else {
+          c += cs;
         }
-        const unsigned long long over = __ballot(((km >> lane) & 1) && c + incl > target);
-        // rounding may leave no lane above u * S: the chunk's last kept id
-        const int l = over ? __ffsll(over) - 1 : 63 - __clzll(km);
-        hit = base + 64 * j + l;
-        break;
       }
-      c += cs;
     }
     if (lane == 0) sh.found = hit >= 0 ? hit : 0x7FFFFFFF;
   }
@@ -442,8 +567,7 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
       if (run <= 1) id = row_sample_regs<1>(lg, V, p.temperature, p.top_k, u, sh);
       else if (run <= 4) id = row_sample_regs<4>(lg, V, p.temperature, p.top_k, u, sh);
       else if (run <= 16) id = row_sample_regs<16>(lg, V, p.temperature, p.top_k, u, sh);
-      else if (run <= 40) id = row_sample_regs<40>(lg, V, p.temperature, p.top_k, u, sh);
-      else if (run <= 100) id = row_sample_regs<100>(lg, V, p.temperature, p.top_k, u, sh);
+      else if (run <= 50) id = row_sample_regs<50>(lg, V, p.temperature, p.top_k, u, sh);
       else id = row_sample(lg, V, p.temperature, p.top_k, u, sh);
     }
   }
