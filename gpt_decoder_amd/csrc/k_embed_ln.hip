@@ -100,6 +100,38 @@ __device__ __forceinline__ void load4(const float* p, float* f) {
   const float4 t = *reinterpret_cast<const float4*>(p);
   f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
 }
+// The same four elements through a range-checked buffer load: offset kLnOut
+// (past every buffer) and a buffer of 0 bytes read zeros, so the load can be
+// issued on every path.
+constexpr uint32_t kLnOut = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ln_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, p ? bytes : 0,
+                                           0x00020000);
+}
+__device__ __forceinline__ void unpack4(uint2 u, const bf16_t*, float* f) {
+  f[0] = to_f32(static_cast<bf16_t>(u.x & 0xffffu));
+  f[1] = to_f32(static_cast<bf16_t>(u.x >> 16));
+  f[2] = to_f32(static_cast<bf16_t>(u.y & 0xffffu));
+  f[3] = to_f32(static_cast<bf16_t>(u.y >> 16));
+}
+__device__ __forceinline__ void unpack4(uint2 u, const f16_t*, float* f) {
+  f[0] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.x & 0xffffu)));
+  f[1] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.x >> 16)));
+  f[2] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.y & 0xffffu)));
+  f[3] = to_f32(__builtin_bit_cast(f16_t, static_cast<uint16_t>(u.y >> 16)));
+}
+template <class T>
+__device__ __forceinline__ void load4_buf(__amdgpu_buffer_rsrc_t r, int c, bool ok, float* f) {
+  const uint32_t off = ok ? (uint32_t)c * sizeof(T) : kLnOut;
+  if constexpr (sizeof(T) == 2) {
+    unpack4(__builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)),
+            static_cast<const T*>(nullptr), f);
+  } else {
+    const float4 t = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w;
+  }
+}
+
 __device__ __forceinline__ void store4(bf16_t* p, const float* f) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
 }
@@ -120,29 +152,34 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   if (i >= M) return;
   const int src = rows ? rows[i] : i;
   const float* xr = x + (size_t)src * ldx;
+  // The row, the gain and the shift are all fetched before the first
+  // reduction, through range-checked buffer loads (issued on every path;
+  // guarded loads were each waited for in turn), so one memory latency is
+  // exposed.
+  const __amdgpu_buffer_rsrc_t rx = ln_rsrc(xr, C * 4);
+  const __amdgpu_buffer_rsrc_t rw = ln_rsrc(w, C * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rb = ln_rsrc(bias, C * (int)sizeof(T));
   float4 v[kLnMaxVec];
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) {
     const int c = j * 256 + lane * 4;
-    v[j] = c < C ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+        rx, c < C ? (uint32_t)c * 4u : kLnOut, 0, 0));
   }
-  // gain and shift fetched with the row, so that one memory latency is
-  // exposed rather than two
   float wv[kLnMaxVec][4], bv[kLnMaxVec][4];
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) {
     const int c = j * 256 + lane * 4;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) wv[j][u] = bv[j][u] = 0.f;
-    if (c < C) {
-      load4(w + c, wv[j]);
-      if (bias) load4(bias + c, bv[j]);
-    }
+    load4_buf<T>(rw, c, c < C, wv[j]);
+    load4_buf<T>(rb, c, c < C, bv[j]);
   }
+  // (keeps the scheduler from sinking the gain and shift loads below the
+  // reductions, which would expose a second memory latency)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-  const float mean = wave_sum(s) / (float)C;
+  const float mean = wave_sum_all(s) / (float)C;
   float q = 0.f;
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) {
@@ -152,7 +189,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
       q += (a * a + b * b) + (d * d + e * e);
     }
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)C + 1e-5f);
+  const float rstd = 1.0f / sqrtf(wave_sum_all(q) / (float)C + 1e-5f);
   T* o = out + (size_t)i * ldo;
 #pragma unroll
   for (int j = 0; j < kLnMaxVec; ++j) {

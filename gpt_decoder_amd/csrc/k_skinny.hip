@@ -87,6 +87,33 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Epilogue inputs of this thread's output elements (idx = tid + q * 64 NWV,
+  // row idx / BN, column idx % BN), fetched before the K loop so that their
+  // latency overlaps it: the bias, the residual being added to, the row's
+  // position and cache row or logits row.  Indices are clamped into range,
+  // so every load is issued on every path.
+  constexpr int NTHR = 64 * NWV;
+  constexpr int EPT = (BM * BN + NTHR - 1) / NTHR;
+  float pb[EPT], pr[EPT];
+  int pp[EPT];
+  int64_t pbase[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int idx = tid + q * NTHR;
+    const int r = min(idx / BN, M - 1), n = min(n0 + idx % BN, N - 1);
+    pb[q] = (EPI != EPI_LOGITS && e.bias) ? to_f32(static_cast<const T*>(e.bias)[n]) : 0.f;
+    pr[q] = EPI == EPI_RESID ? static_cast<const float*>(e.out)[(size_t)r * e.ldo + n] : 0.f;
+    pp[q] = e.row_pos ? e.row_pos[r] : 0;
+    pbase[q] = 0;
+    if constexpr (EPI == EPI_QKV) {
+      const int b = e.row_b ? e.row_b[r] : r;
+      const int64_t base = kv_block_base(e.kv, b, max(pp[q], 0) / kPageTokens);
+      pbase[q] = (n >= e.C && pp[q] >= 0) ? base : -1;
+    } else if constexpr (EPI == EPI_LOGITS) {
+      pbase[q] = e.row_b ? e.row_b[r] : r;   // the sequence's logits row
+    }
+  }
   // (scheduling barriers keep the compiler from sinking the loads towards
   // their use, which would leave fewer pairs in flight)
 #pragma unroll
@@ -127,14 +154,46 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[wave][16 * m + 4 * g4 + v][16 * j + (lane & 15)] = acc[m][j][v];
   __syncthreads();
-  for (int idx = tid; idx < BM * BN; idx += 64 * NWV) {
+  // the epilogue of epi_apply (epilogue.hpp) with the prefetched inputs
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int idx = tid + q * NTHR;
     const int r = idx / BN, c = idx % BN;
     const int n = n0 + c;
-    if (r >= M || n >= N) continue;
-    float v = red[0][r][c];
+    if (idx >= BM * BN || r >= M || n >= N) continue;
+    float acc1 = red[0][r][c];
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) v += red[w][r][c];
-    epi_apply<T, EPI>(e, r, n, v);
+    for (int w = 1; w < NWV; ++w) acc1 += red[w][r][c];
+    if constexpr (EPI == EPI_LOGITS) {
+      if (e.row_pos && pp[q] < 0) continue;
+      static_cast<float*>(e.out)[(size_t)pbase[q] * e.ldo + n] = acc1;
+    } else {
+      float v = acc1;
+      if (e.bias) v += pb[q];
+      if constexpr (EPI == EPI_GELU) {
+        static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(gelu_erf(v));
+      } else if constexpr (EPI == EPI_RESID) {
+        static_cast<float*>(e.out)[(size_t)r * e.ldo + n] = pr[q] + v;
+      } else {   // EPI_QKV
+        const int which = n / e.C;
+        const int cc = n - which * e.C;
+        if (which == 0) {
+          static_cast<T*>(e.out)[(size_t)r * e.ldo + cc] = from_f32<T>(v);
+          continue;
+        }
+        const int p = pp[q];
+        if (p < 0) continue;
+        if (pbase[q] < 0) {   // unmapped block of a paged cache
+          if (e.status) atomicOr(e.status, 4);
+          continue;
+        }
+        const int h = cc / e.hs;
+        const int d = cc - h * e.hs;
+        T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
+        cache[(size_t)(pbase[q] + (int64_t)h * kv_hstride(e.kv) + p % kPageTokens) * e.hs + d] =
+            from_f32<T>(v);
+      }
+    }
   }
 }
 
