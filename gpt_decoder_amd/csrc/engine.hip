@@ -164,7 +164,7 @@ std::map<int, StaticSlot> g_static_slots;
 // Byte offsets of the workspace regions (every region 256-byte aligned).
 struct WsLayout {
   size_t x, h, q, y, f, z, logits, row_b, row_pos, last_rows, last_slot, hist,
-      part, ppart, ids, tok, pos, status, params, done;
+      part, ppart, ids, tok, pos, status, params;
   // one-launch decode exchange buffers (absent: persist_shape == false)
   bool persist_shape = false;
   size_t eq, er, ey, e1, ef, e2, epoch, ecand, dlayers;
@@ -209,8 +209,8 @@ struct ngpt_model {
   PersistLayer* d_layers = nullptr;
   uint64_t *e_qkv = nullptr, *e_rec = nullptr, *e_y = nullptr, *e_x1 = nullptr,
            *e_f = nullptr, *e_x2 = nullptr;
-  uint32_t* epoch = nullptr;
-  uint32_t* done = nullptr;     // departure counter of the one-launch kernel
+  uint32_t* epoch = nullptr;     // the last one-launch forward's exchange epoch
+  uint32_t h_epoch = 0;          // launches of that kernel so far (== *epoch)
   uint64_t* e_cand = nullptr;   // greedy candidates left by the last launch
   bool cand_ok = false;         // the current logits came from that launch
   // the KV cache of the last prefill and the host record of its lengths
@@ -319,7 +319,7 @@ static WsLayout ws_layout(const ngpt_config* cfg) {
   o.ppart = carve((size_t)H * Tb * attn_prefill_split_chunks(Tb) * (hs + 4) * 4);
   o.ids = carve((size_t)cfg->max_prefill_tokens * 4);
   o.tok = carve(Bm * 4); o.pos = carve(Bm * 4); o.status = carve(16);
-  o.params = carve(sizeof(SampleParams)); o.done = carve(16);
+  o.params = carve(sizeof(SampleParams));
   for (int g = 64; g <= persistent_max_grid() && !o.persist_shape; g += 8)
     o.persist_shape = persistent_decode_supported(cfg->dtype, cfg->n_embd, H,
                                                   cfg->n_layer, Tb, 1, g);
@@ -402,7 +402,6 @@ static int create_on(const ngpt_config* cfg, const ngpt_weights* w, void* ws,
   m->tok = (int32_t*)(base + o.tok);
   m->pos = (int32_t*)(base + o.pos); m->status = (int32_t*)(base + o.status);
   m->params = (SampleParams*)(base + o.params);
-  m->done = (uint32_t*)(base + o.done);
 
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -974,7 +973,7 @@ static PersistArgs persist_args(ngpt_model* m, const ngpt_kv* kv) {
   a.logits = m->logits;
   a.e_qkv = m->e_qkv; a.e_rec = m->e_rec; a.e_y = m->e_y;
   a.e_x1 = m->e_x1; a.e_f = m->e_f; a.e_x2 = m->e_x2;
-  a.epoch = m->epoch; a.done = m->done; a.status = m->status;
+  a.epoch = m->epoch; a.status = m->status;
   a.hist = m->hist;
   a.wait_limit = m->h_wait_limit;
   return a;
@@ -1045,6 +1044,7 @@ static SamplerArgs head_args(ngpt_model* m, const ngpt_kv* kv, int mode,
   a.C = m->C;
   a.dtype = m->cfg.dtype;
   a.x = m->x;
+  a.epoch = one_launch(m, kv) ? m->epoch : nullptr;
   return a;
 }
 
@@ -1100,6 +1100,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   if (mode == SAMPLE_STEP && m->h_params.greedy && one_launch(m, kv) && m->cand_ok) {
     PersistArgs a = persist_args(m, kv);
     a.fused = 1;
+    a.ep = ++m->h_epoch;
     a.next_ids = arg_out;
     launch_decode_persistent(a, m->persist_grid, m->stream);
     HIP_TRY(m, hipGetLastError());
@@ -1124,6 +1125,7 @@ static int run_step(ngpt_model* m, ngpt_kv* kv, GraphSlot& g, int mode,
   }
   HIP_TRY(m, hipGraphLaunch(g.exec, m->stream));
   m->cand_ok = one_launch(m, kv);
+  if (m->cand_ok) ++m->h_epoch;   // the head node advanced the word
   for (int b = 0; b < kv->batch; ++b)
     if (m->h_lens[b] < m->h_limit[b]) ++m->h_lens[b];
   return NGPT_OK;

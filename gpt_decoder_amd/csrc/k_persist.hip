@@ -840,7 +840,10 @@ __device__ __forceinline__ void run_role(const PersistArgs& a, float* smem,
 __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ PShared S;
-  const uint32_t ep = *a.epoch + 1u;
+  // Every workgroup reads the same epoch: nothing writes *a.epoch while a
+  // launch that reads it runs (the head node advanced it before), and a
+  // fused launch takes its epoch as an argument.
+  const uint32_t ep = a.fused ? a.ep : *a.epoch;
   // position of the new token: the sampler head node has set pos (< 0:
   // inactive), or, in a fused greedy step, the current length (advanced at
   // the end) while it is below the sequence's limit
@@ -879,18 +882,10 @@ __global__ __launch_bounds__(kThreads) void decode_persistent_kernel(PersistArgs
       tag_store(a.e_cand + 2 * blockIdx.x + 1, __int_as_float(bi), ep);
     }
     if (blockIdx.x == 0 && a.fused && p >= 0 && S.fail == INT_MAX) a.lens[0] = p + 1;
-    // The epoch advances once per launch, by the last workgroup to finish:
-    // every workgroup has read the old value before it arrives here, also
-    // when a wait timed out or the grid was not all resident, so no
-    // workgroup of this launch can tag a word with the next launch's epoch.
-    // (relaxed: the epoch was read at the start and used by every wait
-    // since, and a fence here would write back this XCD's L2)
-    const uint32_t prev = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a fused launch keeps the word in step with the host's count, for the
+    // next head node; no workgroup of this launch reads it
+    if (a.fused && blockIdx.x == 0)
       __hip_atomic_store(a.epoch, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 

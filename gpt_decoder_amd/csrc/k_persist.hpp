@@ -33,9 +33,10 @@ struct PersistArgs {
   float* logits;                // [V]
   // exchange words (fp32 value | epoch << 32), per layer
   uint64_t *e_qkv, *e_rec, *e_y, *e_x1, *e_f, *e_x2;
-  uint32_t* epoch;              // advanced once per launch, by the last
-                                // workgroup to finish
-  uint32_t* done;               // departure counter (zero between launches)
+  uint32_t* epoch;              // the last launch's epoch
+  uint32_t ep;                  // fused: this launch's epoch (the host counts
+                                // launches); otherwise the head node has
+                                // already advanced *epoch and it is read
   int32_t* status;              // bit 2: a wait timed out; bit 1: bad input
   int wait_limit;                // poll passes before a wait gives up (0: default)
 };

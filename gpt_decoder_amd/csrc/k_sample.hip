@@ -525,9 +525,14 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
     int32_t* __restrict__ lens, const int32_t* __restrict__ limit,
     int32_t* __restrict__ status, int32_t* __restrict__ hist, int Tb,
     const void* __restrict__ wte,
-    const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x) {
+    const void* __restrict__ wpe, int C, int dtype, float* __restrict__ x,
+    uint32_t* __restrict__ epoch) {
   __shared__ SampShared sh;
   const int b = blockIdx.x;
+  // ahead of a one-launch forward: advance its exchange epoch (that kernel
+  // starts after this one ends, so all its workgroups read the new value)
+  if (epoch && b == 0 && threadIdx.x == 0)
+    __hip_atomic_store(epoch, *epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool active = true;
   int len = 0;
   if (mode != SAMPLE_ONLY) {
@@ -592,11 +597,11 @@ __global__ __launch_bounds__(kSampThreads) void sampler_kernel(
 }
 
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p) {
-  void* vals[20] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
+  void* vals[21] = {&a.mode, &a.logits, &a.ld, &a.V, &a.uniforms, &a.params,
                     &a.feed_ids, &a.next_ids, &a.tok, &a.pos, &a.lens,
                     &a.limit, &a.status, &a.hist, &a.Tb, &a.wte, &a.wpe, &a.C,
-                    &a.dtype, &a.x};
-  for (int i = 0; i < 20; ++i) a.ptrs[i] = vals[i];
+                    &a.dtype, &a.x, &a.epoch};
+  for (int i = 0; i < 21; ++i) a.ptrs[i] = vals[i];
   p->func = reinterpret_cast<void*>(sampler_kernel);
   p->gridDim = dim3(B);
   p->blockDim = dim3(a.mode == FEED_STEP ? 256 : kSampThreads);
@@ -612,7 +617,7 @@ void launch_sampler(const SamplerArgs& a, int B, hipStream_t s) {
                                        a.params, a.feed_ids, a.next_ids, a.tok,
                                        a.pos, a.lens, a.limit, a.status,
                                        a.hist, a.Tb, a.wte, a.wpe, a.C,
-                                       a.dtype, a.x);
+                                       a.dtype, a.x, a.epoch);
 }
 
 }  // namespace ngpt

@@ -189,7 +189,8 @@ struct SamplerArgs {
   int C = 0;
   int dtype = 0;
   float* x = nullptr;
-  void* ptrs[20] = {};
+  uint32_t* epoch = nullptr;  // advanced by one when the forward is the one-launch kernel
+  void* ptrs[21] = {};
 };
 // Fill a kernel-node description for B rows; `a` must outlive its use.
 void sampler_node_params(SamplerArgs& a, int B, hipKernelNodeParams* p);
