@@ -60,6 +60,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   constexpr int VS = KT + 8;         // sVt row stride (elements)
   constexpr int NKK = HS / 32;       // MFMA steps over the head dimension
   constexpr int ND = HS / 16;        // 16-row output sub-tiles over hs
+  // V^T rows are stored with their key index XORed by 16 * ((dim / 8) % 4):
+  // the eight dims one staging store covers then fall in different LDS
+  // banks, and four consecutive keys stay adjacent for the fragment reads.
+  auto vswz = [](int dim) { return 16 * ((dim >> 3) & 3); };
   __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KS];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[HS * VS];
 
@@ -77,9 +81,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   const int chunk = kch > 0 ? (int)blockIdx.x % nsplit : 0;
   if (chunk >= nch) return;
   const int kt0 = kch > 0 ? chunk * kch : 0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wavefront index as a scalar, so that per-wavefront tests are scalar
+  // branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;                       // lane group 0..3
   const int qrow = q0 + wave * 16 + (lane & 15);  // this lane's query (new row)
+  const int qpos_w = past + q0 + wave * 16;       // the wavefront's first position
   const int qpos = past + qrow;                   // ... and its position
   const int kend = past + len;                    // keys in the cache
   const size_t row0 = (size_t)map.off[b];
@@ -146,12 +154,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rk[st][it][1];
       const uint32_t a[4] = {rv[st][it][0].x, rv[st][it][0].y, rv[st][it][0].z, rv[st][it][0].w};
       const uint32_t b2[4] = {rv[st][it][1].x, rv[st][it][1].y, rv[st][it][1].z, rv[st][it][1].w};
+      const int kx = (2 * kp) ^ vswz(d0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // dims d0+2j (low halves) and d0+2j+1 (high halves) of the two keys
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j) * VS + 2 * kp) =
+        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j) * VS + kx) =
             (a[j] & 0xFFFFu) | (b2[j] << 16);
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j + 1) * VS + 2 * kp) =
+        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j + 1) * VS + kx) =
             (a[j] >> 16) | (b2[j] & 0xFFFF0000u);
       }
     }
@@ -180,34 +189,58 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
         s[t] = Half16<T>::mfma(kf, qf[kk], s[t]);
       }
     }
-    // mask and tile maximum (log2 domain)
-    float tmax = -INFINITY;
+    float alpha, psum = 0.f;
+    if (qpos_w >= k0 + KT - 1) {
+      // every key of the tile is visible to all of the wavefront's queries:
+      // no mask, and the running maximum is finite after this tile
+      float tmax = s[0][0];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + t * 16 + g * 4 + i;
-        const float v = (key <= qpos) ? s[t][i] * sl2 : -INFINITY;
-        s[t][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, lane_xor16(tmax));
-    tmax = fmaxf(tmax, lane_xor32(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-    float psum = 0.f;
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[t][i]);
+      tmax = fmaxf(tmax, lane_xor16(tmax));
+      tmax = fmaxf(tmax, lane_xor32(tmax));
+      // scaling by sl2 > 0 keeps the maximum where it is
+      const float m_new = fmaxf(m_run, tmax * sl2);
+      alpha = exp2_fast(m_run - m_new);   // 0 while m_run is -inf
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = (s[t][i] == -INFINITY) ? 0.f : exp2_fast(s[t][i] - m_new);
-        s[t][i] = p;
-        psum += p;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_fast(fmaf(s[t][i], sl2, -m_new));
+          s[t][i] = p;
+          psum += p;
+        }
+      m_run = m_new;
+    } else {
+      // mask and tile maximum (log2 domain)
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + t * 16 + g * 4 + i;
+          const float v = (key <= qpos) ? s[t][i] : -INFINITY;
+          s[t][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, lane_xor16(tmax));
+      tmax = fmaxf(tmax, lane_xor32(tmax));
+      const float m_new = fmaxf(m_run, tmax * sl2);
+      alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (s[t][i] == -INFINITY) ? 0.f : exp2_fast(fmaf(s[t][i], sl2, -m_new));
+          s[t][i] = p;
+          psum += p;
+        }
+      m_run = m_new;
+    }
     psum += lane_xor16(psum);
     psum += lane_xor32(psum);
     l_run = l_run * alpha + psum;
-    m_run = m_new;
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] *= alpha;
 
@@ -224,9 +257,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16_t* vr = sVt + (d * 16 + (lane & 15)) * VS + u * 32 + g * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const int vrow = d * 16 + (lane & 15), e = u * 32 + g * 4;
+        const bf16_t* vr = sVt + vrow * VS;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (e ^ vswz(vrow)));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((e + 16) ^ vswz(vrow)));
         const vec8 vf = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[d] = Half16<T>::mfma(vf, pf, o[d]);
       }
