@@ -23,6 +23,8 @@
 //                       a second small launch merges the chunks in order.
 #include <math.h>
 
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,46 +51,74 @@ constexpr int kPrefillKch = 8;   // key tiles per chunk when a prefill tile is s
 // chunk leaves its rows' unnormalised state (m, l, o) in part, and
 // attn_prefill_merge combines the chunks in order.  Workgroup x takes query
 // tile ntiles - 1 - x / nsplit (heavy tiles first) and chunk x % nsplit.
+constexpr int kPrefillWaves = 8;   // two wavefronts per 16-row query sub-tile
+
+// Work order of a split batch-1 prefill: the (query tile, chunk) pairs of
+// one head, most key tiles first; workgroup x takes pair it[x / H] of head
+// x % H, so the longest chunks of every head start in the first wave of
+// workgroups and no workgroup is launched without work.  n == 0: the grid is
+// (tiles x chunks, H, B) instead.
+constexpr int kPrefillOrderMax = 128;
+struct PrefillOrder {
+  int n;
+  uint16_t it[kPrefillOrderMax];   // query tile | chunk << 8
+};
+
 template <class T, int HS>
-__global__ __launch_bounds__(256) void attn_prefill_mfma(
+__global__ __launch_bounds__(64 * kPrefillWaves) void attn_prefill_mfma(
     const T* __restrict__ q, int ldq, const T* __restrict__ kc,
     const T* __restrict__ vc, KvMap kvm, RowMap map, int H, int Tb, float scale,
-    T* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part) {
+    T* __restrict__ y, int ldy, int kch, int nsplit, float* __restrict__ part,
+    PrefillOrder ord) {
   typedef typename Half16<T>::vec8 vec8;
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = HS + 8;         // sK row stride (elements)
   constexpr int VS = KT + 8;         // sVt row stride (elements)
   constexpr int NKK = HS / 32;       // MFMA steps over the head dimension
   constexpr int ND = HS / 16;        // 16-row output sub-tiles over hs
+  constexpr int MS = ND * 4 + 4;     // merge record per lane: o, then m, l
   // V^T rows are stored with their key index XORed by 16 * ((dim / 8) % 4):
   // the eight dims one staging store covers then fall in different LDS
   // banks, and four consecutive keys stay adjacent for the fragment reads.
   auto vswz = [](int dim) { return 16 * ((dim >> 3) & 3); };
   __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KS];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[HS * VS];
+  __shared__ __attribute__((aligned(16))) float sM[4 * 64 * MS];
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  int b, h, qt, chunk;
+  if (ord.n > 0) {
+    const int x = blockIdx.x, r = x / H;
+    b = 0;
+    h = x - r * H;
+    qt = ord.it[r] & 0xFF;
+    chunk = ord.it[r] >> 8;
+  } else {
+    b = blockIdx.z;
+    h = blockIdx.y;
+    const int ntiles = (map.off[b + 1] - map.off[b] + 63) / 64;
+    qt = ntiles - 1 - (kch > 0 ? (int)blockIdx.x / nsplit : (int)blockIdx.x);
+    chunk = kch > 0 ? (int)blockIdx.x % nsplit : 0;
+  }
   const int len = map.off[b + 1] - map.off[b];
   const int past = map.past[b];
-  const int ntiles = (len + 63) / 64;
-  const int qt = ntiles - 1 - (kch > 0 ? (int)blockIdx.x / nsplit : (int)blockIdx.x);
   if (qt < 0) return;
   const int q0 = qt * 64;
   // key tiles this query tile meets: 0 .. (its last row's position) / 64
   const int nkt_all = (past + min(q0 + 63, len - 1)) / KT + 1;
   // key tiles [kt0, kt0 + nkt) of this workgroup
   const int nch = kch > 0 ? (nkt_all + kch - 1) / kch : 1;
-  const int chunk = kch > 0 ? (int)blockIdx.x % nsplit : 0;
   if (chunk >= nch) return;
   const int kt0 = kch > 0 ? chunk * kch : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wavefront index as a scalar, so that per-wavefront tests are scalar
-  // branches
+  // branches.  Wavefront w takes query rows 16 (w % 4) .. + 15 of the tile
+  // and keys 32 (w / 4) .. + 31 of every key tile.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4;                       // lane group 0..3
-  const int qrow = q0 + wave * 16 + (lane & 15);  // this lane's query (new row)
-  const int qpos_w = past + q0 + wave * 16;       // the wavefront's first position
+  const int qs = wave & 3, kh = wave >> 2;
+  const int g = lane >> 4;                        // lane group 0..3
+  const int qrow = q0 + qs * 16 + (lane & 15);    // this lane's query (new row)
   const int qpos = past + qrow;                   // ... and its position
+  const int qpos_w = past + q0 + qs * 16;         // the wavefront's first position
   const int kend = past + len;                    // keys in the cache
   const size_t row0 = (size_t)map.off[b];
   const int slot = map.slot[b];
@@ -111,49 +141,44 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
   for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nkt = (nch > 1 ? min(kt0 + kch, nkt_all) : nkt_all) - kt0;
-  // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims; K goes to LDS
+  // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims, of K for the
+  // first four wavefronts and of V for the other four; K goes to LDS
   // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
   // S tiles are in flight in registers.  The loads are range-checked buffer
   // loads issued on every path, through a resource spanning the tile's 64
   // cache rows (one block): keys at or past len (whose cache rows may hold
   // anything), tiles past the last key and unmapped blocks read zeros.
   constexpr int ITEMS = (KT / 2) * (HS / 8);
-  constexpr int IPT = (ITEMS + 255) / 256;
+  static_assert(ITEMS <= 256, "one staging item per thread of each half");
   constexpr int S = 4;
   constexpr uint32_t kOut = 0x80000000u;
-  uint4 rk[S][IPT][2], rv[S][IPT][2];
+  const bool vrole = wave >= 4;
+  const int c = tid & 255;
+  const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
+  const T* src = vrole ? vc : kc;
+  uint4 rs[S][2];
   auto load_tile = [&](int st, int k0) {
     const int64_t bb = k0 < kend ? kv_block_base(kvm, slot, k0 / KT) : -1;
     const size_t r0 = bb < 0 ? 0 : (size_t)(bb + hoff) * HS;
     const int nrec = bb < 0 ? 0 : KT * HS * 2;
-    const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(kc + r0), (short)0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(vc + r0), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(src + r0), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int c = tid + it * 256;
-      const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int key = k0 + 2 * kp + e2;
-        const uint32_t off =
-            (c < ITEMS && key < kend) ? ((uint32_t)(key - k0) * HS + d0) * 2u : kOut;
-        rk[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, off, 0, 0));
-        rv[st][it][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rvs, off, 0, 0));
-      }
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int key = k0 + 2 * kp + e2;
+      const uint32_t off =
+          (c < ITEMS && key < kend) ? ((uint32_t)(key - k0) * HS + d0) * 2u : kOut;
+      rs[st][e2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off, 0, 0));
     }
   };
   auto store_tile = [&](int st) {
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int c = tid + it * 256;
-      if (c >= ITEMS) break;
-      const int kp = c / (HS / 8), d0 = (c % (HS / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rk[st][it][0];
-      *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rk[st][it][1];
-      const uint32_t a[4] = {rv[st][it][0].x, rv[st][it][0].y, rv[st][it][0].z, rv[st][it][0].w};
-      const uint32_t b2[4] = {rv[st][it][1].x, rv[st][it][1].y, rv[st][it][1].z, rv[st][it][1].w};
+    if (c >= ITEMS) return;
+    if (!vrole) {
+      *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rs[st][0];
+      *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rs[st][1];
+    } else {
+      const uint32_t a[4] = {rs[st][0].x, rs[st][0].y, rs[st][0].z, rs[st][0].w};
+      const uint32_t b2[4] = {rs[st][1].x, rs[st][1].y, rs[st][1].z, rs[st][1].w};
       const int kx = (2 * kp) ^ vswz(d0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -175,27 +200,29 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
     store_tile(st);
     __syncthreads();
     load_tile(st, k0 + S * KT);
-    if (t0 + st >= nkt) continue;   // padding of the last group (uniform)
+    if (t0 + st >= nkt) continue;       // padding of the last group (uniform)
+    const int kb = k0 + kh * 32;        // this wavefront's first key
+    if (kb > qpos_w + 15) continue;     // all 32 keys above the diagonal (uniform)
 
-    // S^T for 4 sub-tiles of 16 keys
-    f32x4_t s[4];
+    // S^T for 2 sub-tiles of 16 keys
+    f32x4_t s[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const vec8 kf = *reinterpret_cast<const vec8*>(
-            sK + (t * 16 + (lane & 15)) * KS + kk * 32 + g * 8);
+            sK + (kh * 32 + t * 16 + (lane & 15)) * KS + kk * 32 + g * 8);
         s[t] = Half16<T>::mfma(kf, qf[kk], s[t]);
       }
     }
     float alpha, psum = 0.f;
-    if (qpos_w >= k0 + KT - 1) {
-      // every key of the tile is visible to all of the wavefront's queries:
-      // no mask, and the running maximum is finite after this tile
+    if (qpos_w >= kb + 31) {
+      // every key is visible to all of the wavefront's queries: no mask,
+      // and the running maximum is finite after this step
       float tmax = s[0][0];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[t][i]);
       tmax = fmaxf(tmax, lane_xor16(tmax));
@@ -204,7 +231,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       const float m_new = fmaxf(m_run, tmax * sl2);
       alpha = exp2_fast(m_run - m_new);   // 0 while m_run is -inf
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = exp2_fast(fmaf(s[t][i], sl2, -m_new));
@@ -213,13 +240,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
         }
       m_run = m_new;
     } else {
-      // mask and tile maximum (log2 domain)
+      // mask and maximum (log2 domain)
       float tmax = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = k0 + t * 16 + g * 4 + i;
+          const int key = kb + t * 16 + g * 4 + i;
           const float v = (key <= qpos) ? s[t][i] : -INFINITY;
           s[t][i] = v;
           tmax = fmaxf(tmax, v);
@@ -229,7 +256,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
       const float m_new = fmaxf(m_run, tmax * sl2);
       alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = (s[t][i] == -INFINITY) ? 0.f : exp2_fast(fmaf(s[t][i], sl2, -m_new));
@@ -244,28 +271,55 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] *= alpha;
 
-    // O^T += V^T P^T, 32 keys per MFMA: sub-tiles 2u and 2u+1
+    // O^T += V^T P^T over this wavefront's 32 keys (sub-tiles 0 and 1)
+    vec8 pf;
+    {
+      const uint32_t w0 = Half16<T>::pack2(s[0][0], s[0][1]);
+      const uint32_t w1 = Half16<T>::pack2(s[0][2], s[0][3]);
+      const uint32_t w2 = Half16<T>::pack2(s[1][0], s[1][1]);
+      const uint32_t w3 = Half16<T>::pack2(s[1][2], s[1][3]);
+      pf = __builtin_bit_cast(vec8, make_uint4(w0, w1, w2, w3));
+    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      vec8 pf;
-      {
-        const uint32_t w0 = Half16<T>::pack2(s[2 * u][0], s[2 * u][1]);
-        const uint32_t w1 = Half16<T>::pack2(s[2 * u][2], s[2 * u][3]);
-        const uint32_t w2 = Half16<T>::pack2(s[2 * u + 1][0], s[2 * u + 1][1]);
-        const uint32_t w3 = Half16<T>::pack2(s[2 * u + 1][2], s[2 * u + 1][3]);
-        pf = __builtin_bit_cast(vec8, make_uint4(w0, w1, w2, w3));
-      }
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const int vrow = d * 16 + (lane & 15), e = u * 32 + g * 4;
-        const bf16_t* vr = sVt + vrow * VS;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (e ^ vswz(vrow)));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((e + 16) ^ vswz(vrow)));
-        const vec8 vf = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[d] = Half16<T>::mfma(vf, pf, o[d]);
-      }
+    for (int d = 0; d < ND; ++d) {
+      const int vrow = d * 16 + (lane & 15), e = kh * 32 + g * 4;
+      const bf16_t* vr = sVt + vrow * VS;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vr + (e ^ vswz(vrow)));
+      const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((e + 16) ^ vswz(vrow)));
+      const vec8 vf = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      o[d] = Half16<T>::mfma(vf, pf, o[d]);
     }
   }
+  }
+
+  // The two wavefronts of a query sub-tile merge in key order: the second
+  // leaves its state in LDS, the first folds it into its own and writes.
+  float* mr = sM + ((size_t)qs * 64 + lane) * MS;
+  if (kh == 1) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+      *reinterpret_cast<float4*>(mr + 4 * d) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+    *reinterpret_cast<float2*>(mr + 4 * ND) = make_float2(m_run, l_run);
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float2 ml = *reinterpret_cast<const float2*>(mr + 4 * ND);
+    const float mn = fmaxf(m_run, ml.x);
+    if (mn != -INFINITY) {
+      const float a = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mn);
+      const float c2 = (ml.x == -INFINITY) ? 0.f : exp2_fast(ml.x - mn);
+      l_run = l_run * a + ml.y * c2;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const float4 o2 = *reinterpret_cast<const float4*>(mr + 4 * d);
+        o[d][0] = o[d][0] * a + o2.x * c2;
+        o[d][1] = o[d][1] * a + o2.y * c2;
+        o[d][2] = o[d][2] * a + o2.z * c2;
+        o[d][3] = o[d][3] * a + o2.w * c2;
+      }
+      m_run = mn;
+    }
   }
 
   if (nch > 1) {   // a chunk of a split tile: leave (m, l, o) for the merge
@@ -671,13 +725,38 @@ static void launch_attn_prefill_h(const T* q, int ldq, const T* kc, const T* vc,
   const bool split = part && map.B == 1 && nkt_max > kPrefillKch && ntiles * H < 256;
   const int kch = split ? kPrefillKch : 0;
   const int nsplit = split ? (nkt_max + kPrefillKch - 1) / kPrefillKch : 1;
-  const dim3 grid(ntiles * nsplit, H, map.B);
+  dim3 grid(ntiles * nsplit, H, map.B);
+  PrefillOrder ord;
+  ord.n = 0;
+  if (split) {
+    // every (query tile, chunk) pair of a head with its key-tile count,
+    // longest first (ties: later tiles first); the heads interleave
+    int size[kPrefillOrderMax];
+    int n = 0;
+    for (int qt = ntiles - 1; qt >= 0 && n >= 0; --qt) {
+      const int nkt_all = (past + min(qt * 64 + 63, maxlen - 1)) / 64 + 1;
+      for (int c = 0; c * kch < nkt_all; ++c) {
+        if (n == kPrefillOrderMax || qt > 0xFF || c > 0xFF) { n = -1; break; }
+        size[n] = min(kch, nkt_all - c * kch);
+        ord.it[n++] = (uint16_t)(qt | (c << 8));
+      }
+    }
+    if (n > 0) {
+      for (int i = 1; i < n; ++i)   // stable insertion sort, size descending
+        for (int j = i; j > 0 && size[j] > size[j - 1]; --j) {
+          std::swap(size[j], size[j - 1]);
+          std::swap(ord.it[j], ord.it[j - 1]);
+        }
+      ord.n = n;
+      grid = dim3(n * H, 1, 1);
+    }
+  }
   if (hs == 64)
-    attn_prefill_mfma<T, 64><<<grid, 256, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
-                                                   kch, nsplit, part);
+    attn_prefill_mfma<T, 64><<<grid, 64 * kPrefillWaves, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
+                                                   kch, nsplit, part, ord);
   else
-    attn_prefill_mfma<T, 32><<<grid, 256, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
-                                                   kch, nsplit, part);
+    attn_prefill_mfma<T, 32><<<grid, 64 * kPrefillWaves, 0, s>>>(q, ldq, kc, vc, kv, map, H, Tb, scale, y, ldy,
+                                                   kch, nsplit, part, ord);
   if (split) {
     // rows of single-chunk tiles need no merge: start at the first tile
     // with more than one chunk
