@@ -612,26 +612,29 @@ __global__ __launch_bounds__(256) void attn_decode_rows_kernel(
   const int64_t hoff = (int64_t)h * kv_hstride(kvm);
   const float sl2 = scale * kLog2e;
 
-  // this wavefront's i-th group (zeros past the last one)
+  // this wavefront's i-th group (zeros past the last one), through
+  // range-checked buffer loads over the group's 64-position cache block:
+  // keys past p, groups past the last and unmapped blocks read zeros, and
+  // every load is issued on every path (guarded loads were each waited for
+  // before the next was issued, which emptied the four-group pipeline)
+  constexpr uint32_t kOut = 0x80000000u;
   auto load = [&](int i) {
-    DecGroup g{};
-    if (i < nmine) {
-      const int g0 = (wave + 4 * i) * GK;
-      const int64_t bb = kv_block_base(kvm, b, g0 / kPageTokens);
-      if (bb >= 0) {
-        const int u0 = g0 + kgrp, u1 = g0 + KPP + kgrp;
-        const size_t o0 = (size_t)(bb + hoff + u0 % kPageTokens) * HS + sub * 8;
-        const size_t o1 = (size_t)(bb + hoff + u1 % kPageTokens) * HS + sub * 8;
-        if (u0 <= p) {
-          g.k0 = *reinterpret_cast<const uint4*>(kc + o0);
-          g.v0 = *reinterpret_cast<const uint4*>(vc + o0);
-        }
-        if (u1 <= p) {
-          g.k1 = *reinterpret_cast<const uint4*>(kc + o1);
-          g.v1 = *reinterpret_cast<const uint4*>(vc + o1);
-        }
-      }
-    }
+    DecGroup g;
+    const int g0 = (wave + 4 * i) * GK;
+    const int64_t bb = i < nmine ? kv_block_base(kvm, b, g0 / kPageTokens) : -1;
+    const size_t r0 = bb < 0 ? 0 : (size_t)(bb + hoff) * HS;
+    const int nrec = bb < 0 ? 0 : kPageTokens * HS * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(kc + r0), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(vc + r0), (short)0, nrec, 0x00020000);
+    const int u0 = g0 + kgrp, u1 = g0 + KPP + kgrp;
+    const uint32_t o0 = u0 <= p ? ((uint32_t)(u0 % kPageTokens) * HS + sub * 8) * 2u : kOut;
+    const uint32_t o1 = u1 <= p ? ((uint32_t)(u1 % kPageTokens) * HS + sub * 8) * 2u : kOut;
+    g.k0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, o0, 0, 0));
+    g.v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, o0, 0, 0));
+    g.k1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, o1, 0, 0));
+    g.v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, o1, 0, 0));
     return g;
   };
   // the query first: waiting for it then does not wait for the groups
@@ -650,8 +653,11 @@ __global__ __launch_bounds__(256) void attn_decode_rows_kernel(
     float sc = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) sc = fmaf(qv[j], kf[j], sc);
-#pragma unroll
-    for (int o2 = 1; o2 < LPK; o2 <<= 1) sc += __shfl_xor(sc, o2, 64);
+    // sum over the key's LPK lanes (DPP; every lane of the group gets the
+    // same bits: each step adds a symmetric partner)
+    sc += lane_xor1(sc);
+    sc += lane_xor2(sc);
+    if constexpr (LPK == 8) sc += lane_mirror8(sc);
     if (u <= p) {
       float vf[8];
       Half16<T>::unpack8(vraw, vf);
@@ -669,28 +675,35 @@ __global__ __launch_bounds__(256) void attn_decode_rows_kernel(
     pass(g.k0, g.v0, gk + kgrp);
     pass(g.k1, g.v1, gk + KPP + kgrp);
   };
-  // four groups in flight: process one, then fetch the one four ahead
-  for (int i = 0; i < nmine; i += 4) {
+  // four groups in flight: process one, then fetch the one four ahead, in
+  // whole rounds of four (groups past the last hold no key at or below p
+  // and change nothing), so the loop has one exit and the wait before each
+  // group leaves the three younger groups in flight
+  const int nround = (nmine + 3) / 4;
+  for (int r = 0; r < nround; ++r) {
+    const int i = 4 * r;
     group(g0, i);
     g0 = load(i + 4);
-    if (i + 1 >= nmine) break;
     group(g1, i + 1);
     g1 = load(i + 5);
-    if (i + 2 >= nmine) break;
     group(g2, i + 2);
     g2 = load(i + 6);
-    if (i + 3 >= nmine) break;
     group(g3, i + 3);
     g3 = load(i + 7);
   }
-  // merge the key slots of the wavefront (lanes differing in bits >= LPK)
+  // merge the key slots of the wavefront (lanes differing in bits >= LPK),
+  // through DPP / permlane moves
+  auto xlane = [](float v, int off) {
+    return off == 4 ? __shfl_xor(v, 4, 64)   // (head size 32 only)
+                    : off == 8 ? lane_xor8(v) : off == 16 ? lane_xor16(v) : lane_xor32(v);
+  };
 #pragma unroll
   for (int off = LPK; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off, 64);
-    const float l2 = __shfl_xor(l, off, 64);
+    const float m2 = xlane(m, off);
+    const float l2 = xlane(l, off);
     float o2[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o2[j] = __shfl_xor(o[j], off, 64);
+    for (int j = 0; j < 8; ++j) o2[j] = xlane(o[j], off);
     merge_state(m, l, o, m2, l2, o2, 8);
   }
   if (lane < LPK) {

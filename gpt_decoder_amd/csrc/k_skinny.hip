@@ -28,6 +28,67 @@ namespace ngpt {
 
 constexpr int kSkinnyMaxRows = 64;
 
+// Epilogue inputs of one output element (row r, column n), fetched before the
+// K loop so that their latency overlaps it: the bias, the residual being
+// added to, the row's position and cache row or logits row.  The caller
+// clamps r and n into range, so every load is issued on every path.
+struct SkinnyEpi {
+  float pb, pr;
+  int pp;
+  int64_t pbase;
+};
+template <class T, int EPI>
+__device__ __forceinline__ SkinnyEpi skinny_epi_fetch(const EpiArgs& e, int r, int n) {
+  SkinnyEpi p;
+  p.pb = (EPI != EPI_LOGITS && e.bias) ? to_f32(static_cast<const T*>(e.bias)[n]) : 0.f;
+  p.pr = EPI == EPI_RESID ? static_cast<const float*>(e.out)[(size_t)r * e.ldo + n] : 0.f;
+  p.pp = e.row_pos ? e.row_pos[r] : 0;
+  p.pbase = 0;
+  if constexpr (EPI == EPI_QKV) {
+    const int b = e.row_b ? e.row_b[r] : r;
+    const int64_t base = kv_block_base(e.kv, b, max(p.pp, 0) / kPageTokens);
+    p.pbase = (n >= e.C && p.pp >= 0) ? base : -1;
+  } else if constexpr (EPI == EPI_LOGITS) {
+    p.pbase = e.row_b ? e.row_b[r] : r;   // the sequence's logits row
+  }
+  return p;
+}
+// The epilogue of epi_apply (epilogue.hpp) for one element, acc1 = the dot
+// product, with the prefetched inputs.
+template <class T, int EPI>
+__device__ __forceinline__ void skinny_epi_store(const EpiArgs& e, int r, int n, float acc1,
+                                                 const SkinnyEpi& p) {
+  if constexpr (EPI == EPI_LOGITS) {
+    if (e.row_pos && p.pp < 0) return;
+    static_cast<float*>(e.out)[(size_t)p.pbase * e.ldo + n] = acc1;
+  } else {
+    float v = acc1;
+    if (e.bias) v += p.pb;
+    if constexpr (EPI == EPI_GELU) {
+      static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(gelu_erf(v));
+    } else if constexpr (EPI == EPI_RESID) {
+      static_cast<float*>(e.out)[(size_t)r * e.ldo + n] = p.pr + v;
+    } else {   // EPI_QKV
+      const int which = n / e.C;
+      const int cc = n - which * e.C;
+      if (which == 0) {
+        static_cast<T*>(e.out)[(size_t)r * e.ldo + cc] = from_f32<T>(v);
+        return;
+      }
+      if (p.pp < 0) return;
+      if (p.pbase < 0) {   // unmapped block of a paged cache
+        if (e.status) atomicOr(e.status, 4);
+        return;
+      }
+      const int h = cc / e.hs;
+      const int d = cc - h * e.hs;
+      T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
+      cache[(size_t)(p.pbase + (int64_t)h * kv_hstride(e.kv) + p.pp % kPageTokens) * e.hs + d] =
+          from_f32<T>(v);
+    }
+  }
+}
+
 template <class T, int EPI, int MT, int NT, int NWV, int NP>
 __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     const T* __restrict__ A, int lda, const T* __restrict__ W, int M, int N, int K,
@@ -95,24 +156,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
   // so every load is issued on every path.
   constexpr int NTHR = 64 * NWV;
   constexpr int EPT = (BM * BN + NTHR - 1) / NTHR;
-  float pb[EPT], pr[EPT];
-  int pp[EPT];
-  int64_t pbase[EPT];
+  SkinnyEpi pre[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const int idx = tid + q * NTHR;
-    const int r = min(idx / BN, M - 1), n = min(n0 + idx % BN, N - 1);
-    pb[q] = (EPI != EPI_LOGITS && e.bias) ? to_f32(static_cast<const T*>(e.bias)[n]) : 0.f;
-    pr[q] = EPI == EPI_RESID ? static_cast<const float*>(e.out)[(size_t)r * e.ldo + n] : 0.f;
-    pp[q] = e.row_pos ? e.row_pos[r] : 0;
-    pbase[q] = 0;
-    if constexpr (EPI == EPI_QKV) {
-      const int b = e.row_b ? e.row_b[r] : r;
-      const int64_t base = kv_block_base(e.kv, b, max(pp[q], 0) / kPageTokens);
-      pbase[q] = (n >= e.C && pp[q] >= 0) ? base : -1;
-    } else if constexpr (EPI == EPI_LOGITS) {
-      pbase[q] = e.row_b ? e.row_b[r] : r;   // the sequence's logits row
-    }
+    pre[q] = skinny_epi_fetch<T, EPI>(e, min(idx / BN, M - 1), min(n0 + idx % BN, N - 1));
   }
   // (scheduling barriers keep the compiler from sinking the loads towards
   // their use, which would leave fewer pairs in flight)
@@ -164,36 +212,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     float acc1 = red[0][r][c];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) acc1 += red[w][r][c];
-    if constexpr (EPI == EPI_LOGITS) {
-      if (e.row_pos && pp[q] < 0) continue;
-      static_cast<float*>(e.out)[(size_t)pbase[q] * e.ldo + n] = acc1;
-    } else {
-      float v = acc1;
-      if (e.bias) v += pb[q];
-      if constexpr (EPI == EPI_GELU) {
-        static_cast<T*>(e.out)[(size_t)r * e.ldo + n] = from_f32<T>(gelu_erf(v));
-      } else if constexpr (EPI == EPI_RESID) {
-        static_cast<float*>(e.out)[(size_t)r * e.ldo + n] = pr[q] + v;
-      } else {   // EPI_QKV
-        const int which = n / e.C;
-        const int cc = n - which * e.C;
-        if (which == 0) {
-          static_cast<T*>(e.out)[(size_t)r * e.ldo + cc] = from_f32<T>(v);
-          continue;
-        }
-        const int p = pp[q];
-        if (p < 0) continue;
-        if (pbase[q] < 0) {   // unmapped block of a paged cache
-          if (e.status) atomicOr(e.status, 4);
-          continue;
-        }
-        const int h = cc / e.hs;
-        const int d = cc - h * e.hs;
-        T* cache = static_cast<T*>(which == 1 ? e.kc : e.vc);
-        cache[(size_t)(pbase[q] + (int64_t)h * kv_hstride(e.kv) + p % kPageTokens) * e.hs + d] =
-            from_f32<T>(v);
-      }
-    }
+    skinny_epi_store<T, EPI>(e, r, n, acc1, pre[q]);
   }
 }
 
@@ -256,5 +275,6 @@ bool launch_skinny(int dtype, int epi, const void* A, int lda, const void* W, in
     default: return false;
   }
 }
+
 
 }  // namespace ngpt
