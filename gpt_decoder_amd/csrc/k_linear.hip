@@ -40,22 +40,6 @@ template <> __device__ __forceinline__ float bits_to_f32<f16_t>(uint32_t u16) {
 // 16-bit epilogues), by value so that nothing goes to scratch; columns at or
 // past N get none.
 template <class T>
-__device__ __forceinline__ float4 add_bias4(const T* b, int col, int N, float4 v) {
-  if (col + 3 < N) {
-    const uint2 u = *reinterpret_cast<const uint2*>(b + col);
-    v.x += bits_to_f32<T>(u.x & 0xffffu);
-    v.y += bits_to_f32<T>(u.x >> 16);
-    v.z += bits_to_f32<T>(u.y & 0xffffu);
-    v.w += bits_to_f32<T>(u.y >> 16);
-  } else {
-    v.x += to_f32(b[col]);
-    if (col + 1 < N) v.y += to_f32(b[col + 1]);
-    if (col + 2 < N) v.z += to_f32(b[col + 2]);
-  }
-  return v;
-}
-
-template <class T>
 __device__ __forceinline__ uint2 pack4(float4 v) {
   return make_uint2(Half16<T>::pack2(v.x, v.y), Half16<T>::pack2(v.z, v.w));
 }
@@ -163,31 +147,71 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
   };
 
+  // S K-slabs in flight in registers; slab it goes registers -> LDS buffer
+  // it % 2 -> MFMA.  The trip count is rounded up to a multiple of S (the
+  // extra slabs are zeros).
+  const int nk = NKC > 0 ? NKC : K / BK;
+  const int nkp = ((nk + S - 1) / S) * S;
+  constexpr int kUnroll = NKC > 0 ? 64 : 1;   // whole loop when K is known
+#pragma unroll
+  for (int st = 0; st < S; ++st) gload(st, st * BK);
+
   // Epilogue inputs that do not depend on the product are fetched before
-  // the K loop, which hides their latency: the rows' cache positions (QKV)
-  // and, for small tiles, the residual values being added to (RESID).
+  // the K loop (after its first slabs' loads are issued), which hides their
+  // latency: the rows' cache positions (QKV), the bias of the 16-bit
+  // epilogues and, for small tiles, the residual values being added to
+  // (RESID).  Every fetch is a range-checked buffer load issued on every
+  // path: loads behind per-lane branches were each waited for in turn,
+  // before the K loop's first loads were even issued.
   // (kSwap: lane l holds output row (l % 16) of each row fragment at the
   // four consecutive columns 4 * (l / 16) + i of each column fragment;
   // otherwise column (l % 16) at rows 4 * (l / 16) + i)
   auto out_row = [&](int i) { return m0 + wm * WM + i * 16 + (lane & 15); };
   auto out_col = [&](int j) { return n0 + wn * WN + j * 16 + (lane >> 4) * 4; };
-  // QKV: cache row (of hs elements, head 0) of each output row's position,
-  // -1 for inactive rows and unmapped blocks (the latter flagged)
-  int64_t rrow[TM];
+  auto rsrc = [](const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                             p ? (int)bytes : 0, 0x00020000);
+  };
+  // QKV: each output row's position and sequence (the cache rows are
+  // formed after the K loop, where a paged cache's table read costs no
+  // wait in front of the loop)
+  constexpr bool kQkv = EPI == EPI_QKV;
+  int pv[kQkv ? TM : 1], sv[kQkv ? TM : 1];
   constexpr bool kPreRes = (EPI == EPI_RESID) && TM * TN * 4 <= 16;
   float res[kPreRes ? TM : 1][kPreRes ? TN : 1][4];
-  if constexpr (EPI == EPI_QKV) {
+  constexpr bool kPreBias = (EPI == EPI_QKV || EPI == EPI_GELU);
+  float bias4[kPreBias ? TN : 1][4];
+  if constexpr (kQkv) {
+    const __amdgpu_buffer_rsrc_t rp = rsrc(e.row_pos, (uint32_t)M * 4u);
+    const __amdgpu_buffer_rsrc_t rbq = rsrc(e.row_b, (uint32_t)M * 4u);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = min(out_row(i), M - 1);
-      const int p = e.row_pos[row];
-      const int sq = e.row_b ? e.row_b[row] : row;
-      const int64_t base = p >= 0 ? kv_block_base(e.kv, sq, p / kPageTokens) : -1;
-      if (p >= 0 && base < 0 && e.status) atomicOr(e.status, 4);
-      rrow[i] = base < 0 ? -1 : base + p % kPageTokens;
+      const uint32_t off = (uint32_t)min(out_row(i), M - 1) * 4u;
+      pv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0);
+      sv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rbq, off, 0, 0);
     }
   }
+  if constexpr (kPreBias) {
+    const __amdgpu_buffer_rsrc_t rb16 = rsrc(e.bias, (uint32_t)N * 2u);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int col = out_col(j) + v;
+        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(
+            rb16, col < N ? (uint32_t)col * 2u : kOut, 0, 0);
+        bias4[j][v] = bits_to_f32<T>(u & 0xffffu);
+      }
+  }
+  float biasr[kPreRes ? TN : 1];   // RESID: the bias of this lane's column
   if constexpr (kPreRes) {
+    const __amdgpu_buffer_rsrc_t rb16 = rsrc(e.bias, (uint32_t)N * 2u);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + j * 16 + (lane & 15);
+      biasr[j] = bits_to_f32<T>(__builtin_amdgcn_raw_buffer_load_b16(
+                     rb16, col < N ? (uint32_t)col * 2u : kOut, 0, 0) & 0xffffu);
+    }
     const float* o = static_cast<const float*>(e.out);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -201,14 +225,6 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         }
   }
 
-  // S K-slabs in flight in registers; slab it goes registers -> LDS buffer
-  // it % 2 -> MFMA.  The trip count is rounded up to a multiple of S (the
-  // extra slabs are zeros).
-  const int nk = NKC > 0 ? NKC : K / BK;
-  const int nkp = ((nk + S - 1) / S) * S;
-  constexpr int kUnroll = NKC > 0 ? 64 : 1;   // whole loop when K is known
-#pragma unroll
-  for (int st = 0; st < S; ++st) gload(st, st * BK);
 #pragma unroll kUnroll
   for (int it0 = 0; it0 < nkp; it0 += S) {
 #pragma unroll
@@ -242,6 +258,34 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   }
 
   if constexpr (EPI == EPI_QKV) {
+    // cache row (of hs elements, head 0) of each output row's position, -1
+    // for inactive rows and unmapped blocks (the latter flagged); the block
+    // table of a paged cache is read here, the entries of inactive rows not
+    // at all (offset past the end)
+    int64_t rrow[TM];
+    const __amdgpu_buffer_rsrc_t rt = rsrc(e.kv.table, 0x7FFFFFF0u);
+    int pg[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int sq = e.row_b ? sv[i] : min(out_row(i), M - 1);
+      sv[i] = sq;
+      const uint32_t off = pv[i] >= 0 ? (uint32_t)(sq * e.kv.nblk + pv[i] / kPageTokens) * 4u
+                                       : kOut;
+      pg[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int p = pv[i];
+      int64_t base = -1;
+      if (p >= 0) {
+        if (!e.kv.table)
+          base = (int64_t)sv[i] * e.kv.H * e.kv.Tb + (int64_t)(p / kPageTokens) * kPageTokens;
+        else if ((uint32_t)pg[i] < (uint32_t)e.kv.npages)
+          base = (int64_t)pg[i] * e.kv.H * kPageTokens;
+      }
+      if (p >= 0 && base < 0 && e.status) atomicOr(e.status, 4);
+      rrow[i] = base < 0 ? -1 : base + p % kPageTokens;
+    }
     // columns -> q / k / v, head, dim once per column fragment (the four
     // columns of a lane lie in one head: 4 | hs, and 4 | ldo = n_embd)
 #pragma unroll
@@ -258,7 +302,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         const int row = out_row(i);
         if (row >= M) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (e.bias) v = add_bias4(static_cast<const T*>(e.bias), col, N, v);
+        if (e.bias) v = make_float4(v.x + bias4[j][0], v.y + bias4[j][1], v.z + bias4[j][2],
+                                    v.w + bias4[j][3]);
         const uint2 packed = pack4<T>(v);
         if (which == 0) {
           *reinterpret_cast<uint2*>(static_cast<T*>(e.out) + (size_t)row * e.ldo + c) = packed;
@@ -276,7 +321,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         const int row = out_row(i), col = out_col(j);
         if (row >= M || col >= N) continue;
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (e.bias) v = add_bias4(static_cast<const T*>(e.bias), col, N, v);
+        if (e.bias) v = make_float4(v.x + bias4[j][0], v.y + bias4[j][1], v.z + bias4[j][2],
+                                    v.w + bias4[j][3]);
         v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
         T* o = static_cast<T*>(e.out) + (size_t)row * e.ldo + col;
         if (vec && col + 3 < N) {
@@ -301,7 +347,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
           if (row >= M) continue;
           if constexpr (kPreRes) {
             float val = acc[i][j][v];
-            if (e.bias) val += to_f32(static_cast<const T*>(e.bias)[col]);
+            if (e.bias) val += biasr[j];
             static_cast<float*>(e.out)[(size_t)row * e.ldo + col] = res[i][j][v] + val;
           } else {
             epi_apply<T, EPI>(e, row, col, acc[i][j][v]);
