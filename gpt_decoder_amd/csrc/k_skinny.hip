@@ -6,8 +6,10 @@
 // c_proj and the tied lm_head of the SDK guide's GPT class), with the same
 // per-element epilogues.
 //
-// A workgroup owns a strip of 16 * NT output columns and all M rows (16 * MT,
-// zero-padded).  K goes in pairs of MFMA steps (64 values); wavefront w of
+// A workgroup owns a strip of 16 * NT output columns and a block of 16 * MT
+// rows (blockIdx.y; rows past M read zeros); narrow layers (the n_embd-wide
+// projections) split the rows over several workgroups so that enough CUs
+// stream the weights.  K goes in pairs of MFMA steps (64 values); wavefront w of
 // the NWV takes the NP consecutive pairs starting at pair w * NP (pairs past
 // K read zeros).  Each 16-row operand fragment of a pair is fetched with two
 // loads that cover 8 rows x 128 bytes each (whole cache lines; a load in the
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   bf16_t* stage = reinterpret_cast<bf16_t*>(smem) + wave * STAGE;
   const int n0 = blockIdx.x * BN;
+  const int r0 = blockIdx.y * BM;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(A), (short)0, (int)((uint32_t)M * (uint32_t)lda * 2u), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
     for (int u = 0; u < 2; ++u) {
       const int r = 8 * u + frow;
       if (f < MT) {
-        const int row = 16 * f + r;
+        const int row = r0 + 16 * f + r;
         off[f][u] = row < M ? ((uint32_t)row * (uint32_t)lda + 8u * fch) * 2u : kOut;
       } else {
         const int n = n0 + 16 * (f - MT) + r;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const int idx = tid + q * NTHR;
-    pre[q] = skinny_epi_fetch<T, EPI>(e, min(idx / BN, M - 1), min(n0 + idx % BN, N - 1));
+    pre[q] = skinny_epi_fetch<T, EPI>(e, min(r0 + idx / BN, M - 1), min(n0 + idx % BN, N - 1));
   }
   // (scheduling barriers keep the compiler from sinking the loads towards
   // their use, which would leave fewer pairs in flight)
@@ -206,12 +209,12 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const int idx = tid + q * NTHR;
-    const int r = idx / BN, c = idx % BN;
-    const int n = n0 + c;
+    const int rl = idx / BN, c = idx % BN;
+    const int r = r0 + rl, n = n0 + c;
     if (idx >= BM * BN || r >= M || n >= N) continue;
-    float acc1 = red[0][r][c];
+    float acc1 = red[0][rl][c];
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) acc1 += red[w][r][c];
+    for (int w = 1; w < NWV; ++w) acc1 += red[w][rl][c];
     skinny_epi_store<T, EPI>(e, r, n, acc1, pre[q]);
   }
 }
@@ -229,13 +232,21 @@ static bool skinny_t(const T* a, int lda, const T* w, int M, int N, int K, const
   const int npairs = K / 64;
   const int nw = (npairs > 12 || grid < 256) ? 8 : 4;
   const int np = (npairs + nw - 1) / nw;
-  const bool m2 = M <= 32;
+  // rows per workgroup: all of them (up to 64) when the column strips
+  // alone fill the chip, else blocks of 32 or 16 rows, so that narrow
+  // layers (n_embd outputs: 48 strips at GPT-2 small) are streamed by more
+  // CUs; each workgroup then reads a smaller share of the activation rows
+  int mt = M > 32 ? 4 : M > 16 ? 2 : 1;
+  while (mt > 1 && grid * ((M + 16 * mt - 1) / (16 * mt)) < 256) mt /= 2;
+  const dim3 g2(grid, (M + 16 * mt - 1) / (16 * mt));
 #define NGPT_SKINNY(NWV, NP)                                                                   \
   do {                                                                                         \
-    if (m2)                                                                                    \
-      gemm_skinny_kernel<T, EPI, 2, NT, NWV, NP><<<grid, 64 * NWV, 0, s>>>(a, lda, w, M, N, K, e); \
+    if (mt == 1)                                                                               \
+      gemm_skinny_kernel<T, EPI, 1, NT, NWV, NP><<<g2, 64 * NWV, 0, s>>>(a, lda, w, M, N, K, e); \
+    else if (mt == 2)                                                                          \
+      gemm_skinny_kernel<T, EPI, 2, NT, NWV, NP><<<g2, 64 * NWV, 0, s>>>(a, lda, w, M, N, K, e); \
     else                                                                                       \
-      gemm_skinny_kernel<T, EPI, 4, NT, NWV, NP><<<grid, 64 * NWV, 0, s>>>(a, lda, w, M, N, K, e); \
+      gemm_skinny_kernel<T, EPI, 4, NT, NWV, NP><<<g2, 64 * NWV, 0, s>>>(a, lda, w, M, N, K, e); \
     return true;                                                                               \
   } while (0)
   if (nw == 4) {
