@@ -93,7 +93,7 @@ __device__ __forceinline__ void kloop_dma(__amdgpu_buffer_rsrc_t ra_rs, __amdgpu
                                           int lda, int K, int M, int N, int m0, int n0,
                                           f32x4_t (&acc)[TM][TN]) {
   typedef typename Half16<T>::vec8 vec8;
-  static_assert(NS >= 2 && NS <= 4 && NK >= 1, "stages / slabs");
+  static_assert(NS >= 2 && NS <= 4 && NK >= 0, "stages / slabs (NK = 0: K / 64 at run time)");
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int PA = BM / 32, PB = BN / 32;   // load instructions per wavefront per slab
   constexpr int P = PA + PB;
@@ -134,17 +134,13 @@ __device__ __forceinline__ void kloop_dma(__amdgpu_buffer_rsrc_t ra_rs, __amdgpu
       dma16(rb_rs, base + BM * 128 + (wave * PB + j) * 1024, boff[j] == kOut ? kOut : boff[j] + kb);
   };
 
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (i < NK) issue(i);
-#pragma unroll
-  for (int it = 0; it < NK; ++it) {
-    const int last = (it + NS - 2 < NK - 1) ? it + NS - 2 : NK - 1;
+  auto slab = [&](int it, int nk) {
+    const int last = (it + NS - 2 < nk - 1) ? it + NS - 2 : nk - 1;
     wait_vmcnt_stages<P>(last - it);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + NS - 1 < NK) issue(it + NS - 1);
+    if (it + NS - 1 < nk) issue(it + NS - 1);
     const char* sa = stage(it);
     const char* sb = sa + BM * 128;
 #pragma unroll
@@ -167,6 +163,25 @@ __device__ __forceinline__ void kloop_dma(__amdgpu_buffer_rsrc_t ra_rs, __amdgpu
         for (int j = 0; j < TN; ++j)
           acc[i][j] = kSwap ? Half16<T>::mfma(bfr[j], af[i], acc[i][j])
                             : Half16<T>::mfma(af[i], bfr[j], acc[i][j]);
+    }
+  };
+  if constexpr (NK > 0) {
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < NK) issue(i);
+#pragma unroll
+    for (int it = 0; it < NK; ++it) slab(it, NK);
+  } else {
+    // K known at run time: the loop goes in rounds of NS slabs, so that
+    // each slab's stage is still a compile-time constant
+    const int nk = K / 64;
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < nk) issue(i);
+    for (int it0 = 0; it0 < nk; it0 += NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        if (it0 + st < nk) slab(it0 + st, nk);
     }
   }
 }
@@ -922,6 +937,35 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU;
   const bool wide = kWideEpi && M > 64 && cost(128, 96) < cost(big ? 128 : 64, 64);
   const int g = wide ? tiles(128, 96) : big ? tiles(128, 64) : tiles(64, 64);
+  constexpr int kCUs = 256;
+  // Direct-to-LDS K loop (kloop_dma) for the 128x96 tiles: three stages
+  // when the grid is one round of workgroups (c_attn / c_fc at 1024 rows,
+  // 13.1 -> 9.8 and 13.6 -> 10.5 us); two (57 KB of LDS, two workgroups
+  // per CU) when it runs several rounds, e.g. the XL shape at 16384 rows:
+  // c_attn 603 -> 429 us, c_fc 802 -> 559 us, bit-identical.
+  if constexpr (kWideEpi) {
+    if (wide) {
+      if (K == 768) {
+        if (g > kCUs) gemm_mfma_kernel<T, 128, 96, EPI, 2, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+        else gemm_mfma_kernel<T, 128, 96, EPI, 3, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      } else {
+        gemm_mfma_kernel<T, 128, 96, EPI, 2, 0, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      }
+      return;
+    }
+  }
+  // Residual projections over many rounds of 64x64 tiles (n_embd up to
+  // 2048 inputs): the same loop, three stages, three workgroups per CU
+  // (XL c_proj at 16384 rows 242 -> 202 us).  At 1024 rows and for the
+  // 4 n_embd-input MLP projection the register path below is faster.
+  if constexpr (EPI == EPI_RESID) {
+    const int g64 = tiles(64, 64);
+    if (M > 64 && g64 >= 4 * kCUs && K <= 2048) {
+      if (K == 768) gemm_mfma_kernel<T, 64, 64, EPI, 3, 12, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 3, 0, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      return;
+    }
+  }
   // (only the pairs a block issues: c_attn, c_fc, c_proj at K = 768, the
   // MLP projection at K = 3072)
   constexpr bool k768 = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_RESID;
@@ -929,15 +973,8 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   bool done = false;
   if constexpr (k768) {
     if (K == 768) {
-      if constexpr (kWideEpi) {
-        // (direct-to-LDS K loop, three stages: 13.1 -> 9.8 us for c_attn's
-        // shape and 13.6 -> 10.5 us for c_fc's at 1024 rows, bit-identical)
-        if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 3, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      }
-      if (!wide) {
-        if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        else gemm_mfma_kernel<T, 64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      }
+      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 64, 64, EPI, 4, 12><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
       done = true;
     }
   }
@@ -949,13 +986,8 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
     }
   }
   if (!done) {
-    if constexpr (kWideEpi) {
-      if (wide) gemm_mfma_kernel<T, 128, 96, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    }
-    if (!wide) {
-      if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else gemm_mfma_kernel<T, 64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-    }
+    if (big) gemm_mfma_kernel<T, 128, 64, EPI, 4><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+    else gemm_mfma_kernel<T, 64, 64, EPI, 8><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
   }
 }
 
