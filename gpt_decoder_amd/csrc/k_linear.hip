@@ -931,10 +931,11 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   // compile-time constants, so the K loop is fully unrolled: at every trip
   // of a rolled loop the compiler waits for all loads in flight.
   const bool big = M > 64 && cost(128, 64) <= cost(64, 64);
-  // 128x96 tiles for c_attn and c_fc when they cost less (at 1024 rows of
-  // GPT-2 small: 192 and 256 tiles, one round; measured 2-2.5 us faster
-  // per launch than 128x64)
-  constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU;
+  // 128x96 tiles for c_attn, c_fc and an all-position lm_head when they
+  // cost less (at 1024 rows of GPT-2 small: 192 and 256 tiles, one round;
+  // measured 2-2.5 us faster per launch than 128x64; the evaluation
+  // forward's lm_head over 1024 rows: 1253 -> 1208 us for the whole pass)
+  constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_LOGITS;
   const bool wide = kWideEpi && M > 64 && cost(128, 96) < cost(big ? 128 : 64, 64);
   const int g = wide ? tiles(128, 96) : big ? tiles(128, 64) : tiles(64, 64);
   constexpr int kCUs = 256;
