@@ -955,15 +955,22 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
       return;
     }
   }
-  // Residual projections over many rounds of 64x64 tiles (n_embd up to
-  // 2048 inputs): the same loop, three stages, three workgroups per CU
-  // (XL c_proj at 16384 rows 242 -> 202 us).  At 1024 rows and for the
-  // 4 n_embd-input MLP projection the register path below is faster.
+  // Residual projections over many rounds of tiles: the same loop, with
+  // 64x64 tiles and three stages (three workgroups per CU) up to 2048
+  // inputs (XL c_proj at 16384 rows 242 -> 202 us), 128x96 tiles and two
+  // stages beyond 4 n_embd = 3072 inputs (XL MLP c_proj 802 -> 681 us;
+  // the XL prefill 103.9 -> 98.3 ms).  At 1024 rows, and for 3072 inputs
+  // (the 124M MLP projection), the register path below was faster in the
+  // whole prefill.
   if constexpr (EPI == EPI_RESID) {
-    const int g64 = tiles(64, 64);
+    const int g64 = tiles(64, 64), g96 = tiles(128, 96);
     if (M > 64 && g64 >= 4 * kCUs && K <= 2048) {
       if (K == 768) gemm_mfma_kernel<T, 64, 64, EPI, 3, 12, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
       else gemm_mfma_kernel<T, 64, 64, EPI, 3, 0, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      return;
+    }
+    if (M > 64 && g96 >= 4 * kCUs && K > 3072) {
+      gemm_mfma_kernel<T, 128, 96, EPI, 2, 0, true><<<g96, 256, 0, s>>>(a, lda, w, M, N, K, e);
       return;
     }
   }
