@@ -88,14 +88,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // barrier (their loads of slab it are then complete); the slab it + NS - 1
 // loads then go into the stage that slab it - 1 used, which every
 // wavefront has finished reading by that barrier.
-template <class T, int BM, int BN, int NS, int NK, bool kSwap, int TM, int TN>
+template <class T, int BM, int BN, int NS, int NK, bool kSwap, int TM, int TN, int NW = 4>
 __device__ __forceinline__ void kloop_dma(__amdgpu_buffer_rsrc_t ra_rs, __amdgpu_buffer_rsrc_t rb_rs,
                                           int lda, int K, int M, int N, int m0, int n0,
                                           f32x4_t (&acc)[TM][TN]) {
   typedef typename Half16<T>::vec8 vec8;
   static_assert(NS >= 2 && NS <= 4 && NK >= 0, "stages / slabs (NK = 0: K / 64 at run time)");
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int PA = BM / 32, PB = BN / 32;   // load instructions per wavefront per slab
+  constexpr int WM = BM / (NW / 2), WN = BN / 2;   // NW wavefronts as (NW / 2) x 2
+  constexpr int PA = BM / (8 * NW), PB = BN / (8 * NW);   // load instructions per wavefront per slab
+  static_assert(PA * 8 * NW == BM && PB * 8 * NW == BN, "whole 8-row loads per wavefront");
   constexpr int P = PA + PB;
   constexpr int SB = (BM + BN) * 128;         // bytes per stage
   constexpr uint32_t kOut = 0x80000000u;      // offset past every buffer: reads 0
@@ -212,14 +213,15 @@ __device__ __forceinline__ void kloop_dma(__amdgpu_buffer_rsrc_t ra_rs, __amdgpu
 // read-modify-write of the residual).  Both operands are fed with the same K
 // order, so the dot products do not depend on how the hardware numbers K.
 // ---------------------------------------------------------------------------
-template <class T, int BM, int BN, int EPI, int S, int NKC = 0, bool DMA = false>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+template <class T, int BM, int BN, int EPI, int S, int NKC = 0, bool DMA = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(
     const T* __restrict__ A, int lda, const T* __restrict__ W, int M,
     int N, int K, EpiArgs e) {
   typedef typename Half16<T>::vec8 vec8;
   constexpr int BK = 64;
   constexpr int LDS = BK + 8;  // padded row stride (elements)
-  constexpr int WM = BM / 2, WN = BN / 2;
+  static_assert(NW == 4 || (NW == 8 && DMA), "eight wavefronts only with the direct-to-LDS loop");
+  constexpr int WM = BM / (NW / 2), WN = BN / 2;   // NW wavefronts as (NW / 2) x 2
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ACH = BM * 8 / 256;  // 16-byte chunks per thread (A tile)
   constexpr int BCH = BN * 8 / 256;
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   }
 
   if constexpr (DMA) {
-    kloop_dma<T, BM, BN, S, NKC, kSwap, TM, TN>(ra_rs, rb_rs, lda, K, M, N, m0, n0, acc);
+    kloop_dma<T, BM, BN, S, NKC, kSwap, TM, TN, NW>(ra_rs, rb_rs, lda, K, M, N, m0, n0, acc);
   } else {
     __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS];
     __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS];
@@ -933,44 +935,42 @@ static void dispatch_mfma(const T* a, int lda, const T* w, int M, int N, int K,
   const bool big = M > 64 && cost(128, 64) <= cost(64, 64);
   // 128x96 tiles for c_attn, c_fc and an all-position lm_head when they
   // cost less (at 1024 rows of GPT-2 small: 192 and 256 tiles, one round;
-  // measured 2-2.5 us faster per launch than 128x64; the evaluation
-  // forward's lm_head over 1024 rows: 1253 -> 1208 us for the whole pass)
+  // measured 2-2.5 us faster per launch than 128x64)
   constexpr bool kWideEpi = EPI == EPI_QKV || EPI == EPI_GELU || EPI == EPI_LOGITS;
   const bool wide = kWideEpi && M > 64 && cost(128, 96) < cost(big ? 128 : 64, 64);
   const int g = wide ? tiles(128, 96) : big ? tiles(128, 64) : tiles(64, 64);
   constexpr int kCUs = 256;
-  // Direct-to-LDS K loop (kloop_dma) for the 128x96 tiles: three stages
-  // when the grid is one round of workgroups (c_attn / c_fc at 1024 rows,
-  // 13.1 -> 9.8 and 13.6 -> 10.5 us); two (57 KB of LDS, two workgroups
-  // per CU) when it runs several rounds, e.g. the XL shape at 16384 rows:
-  // c_attn 603 -> 429 us, c_fc 802 -> 559 us, bit-identical.
-  if constexpr (kWideEpi) {
-    if (wide) {
-      if (K == 768) {
-        if (g > kCUs) gemm_mfma_kernel<T, 128, 96, EPI, 2, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-        else gemm_mfma_kernel<T, 128, 96, EPI, 3, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      } else {
-        gemm_mfma_kernel<T, 128, 96, EPI, 2, 0, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+  // Grids of several rounds (batched prefills, the XL shape, the
+  // all-position lm_head): eight-wavefront tiles with the direct-to-LDS K
+  // loop (kloop_dma), two stages, two wavefronts per SIMD: 192x128 for the
+  // 16-bit epilogues at 4096 rows or more, else 128x128.  Against the
+  // four-wavefront 128x96 tiles at 16384 rows of the XL shape: c_attn
+  // 452 -> 354 us, c_fc 600 -> 477 us, c_proj 201 -> 151 us, MLP c_proj
+  // 674 -> 525 us; batch-64 prompts (17408 rows): c_fc 171 -> 133 us, MLP
+  // c_proj 205 -> 121 us; bit-identical.  Whole passes: XL batch-32 prefill
+  // 98.8 -> 87.3 ms, batch-64 prefill 8.98 -> 7.72 ms, the 1024-position
+  // evaluation forward (its lm_head) 1215 -> 1168 us.
+  if (M > 64 && tiles(128, 128) > kCUs) {
+    if constexpr (kWideEpi) {
+      if (M >= 4096) {
+        gemm_mfma_kernel<T, 192, 128, EPI, 2, 0, true, 8><<<tiles(192, 128), 512, 0, s>>>(
+            a, lda, w, M, N, K, e);
+        return;
       }
+    }
+    if constexpr (kWideEpi || EPI == EPI_RESID) {
+      gemm_mfma_kernel<T, 128, 128, EPI, 2, 0, true, 8><<<tiles(128, 128), 512, 0, s>>>(
+          a, lda, w, M, N, K, e);
       return;
     }
   }
-  // Residual projections over many rounds of tiles: the same loop, with
-  // 64x64 tiles and three stages (three workgroups per CU) up to 2048
-  // inputs (XL c_proj at 16384 rows 242 -> 202 us), 128x96 tiles and two
-  // stages beyond 4 n_embd = 3072 inputs (XL MLP c_proj 802 -> 681 us;
-  // the XL prefill 103.9 -> 98.3 ms).  At 1024 rows, and for 3072 inputs
-  // (the 124M MLP projection), the register path below was faster in the
-  // whole prefill.
-  if constexpr (EPI == EPI_RESID) {
-    const int g64 = tiles(64, 64), g96 = tiles(128, 96);
-    if (M > 64 && g64 >= 4 * kCUs && K <= 2048) {
-      if (K == 768) gemm_mfma_kernel<T, 64, 64, EPI, 3, 12, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      else gemm_mfma_kernel<T, 64, 64, EPI, 3, 0, true><<<g64, 256, 0, s>>>(a, lda, w, M, N, K, e);
-      return;
-    }
-    if (M > 64 && g96 >= 4 * kCUs && K > 3072) {
-      gemm_mfma_kernel<T, 128, 96, EPI, 2, 0, true><<<g96, 256, 0, s>>>(a, lda, w, M, N, K, e);
+  // One round of 128x96 tiles (c_attn / c_fc at 1024 rows): the same loop
+  // with four wavefronts and three stages (13.1 -> 9.8 and 13.6 -> 10.5 us
+  // against the register-staged loop).
+  if constexpr (kWideEpi) {
+    if (wide) {
+      if (K == 768) gemm_mfma_kernel<T, 128, 96, EPI, 3, 12, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
+      else gemm_mfma_kernel<T, 128, 96, EPI, 3, 0, true><<<g, 256, 0, s>>>(a, lda, w, M, N, K, e);
       return;
     }
   }
