@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (TOL_BF16, TOL_F32, dev_f64, dev_i32, draws_must_agree, gpu_prefill,
+from gpu_common import (TOL_BF16, TOL_F32, check_cache_stage, dev_f64, dev_i32, draws_must_agree,
+                        gpu_prefill, kv_layer_bits, make_exact_oracle,
                         log, make_model, make_oracle, max_abs, need_gpu, tol_for)
 
 pytestmark = pytest.mark.gpu
@@ -540,3 +541,42 @@ def test_one_launch_decode_stops_at_the_sequence_limit():
     assert m.device_status() == 0
     assert worst < TOL_BF16
     m.close()
+
+
+def test_eight_wavefront_tiles_mid_size_prefill():
+    """A packed prefill of about 2000 rows at n_embd 768 runs c_attn and c_fc
+    through the eight-wavefront 128x128 tiles (more than one round of them,
+    fewer than 4096 rows), with a ragged last row tile: every row's layer-0
+    K and V against the oracle's first-block steps, and the last-position
+    logits of every sequence against both oracle modes."""
+    need_gpu()
+    w = synth.Workload("edge_tiles_768", 12, 1, 12, 768, 512, 300, 300, True, "bf16",
+                       batch=4, prompt_len=8)
+    W = synth.make_weights(w, gamma_std=0.1)
+    rng = np.random.default_rng(77)
+    lens = np.array([512, 512, 511, 500], np.int32)          # 2035 rows
+    ids = rng.integers(0, w.vocab_size, (4, 512)).astype(np.int32)
+    m = make_model(w, W, max_prefill_tokens=int(lens.sum()))
+    kv = m.new_kv(4)
+    got = gpu_prefill(m, kv, ids, lens)
+    lw = W["layers"][0]
+    C, hs = w.n_embd, w.n_embd // w.n_head
+    kb, vb = kv_layer_bits(kv, w, 0, "k"), kv_layer_bits(kv, w, 0, "v")
+    worst = 0.0
+    for b in range(4):
+        L0 = int(lens[b])
+        x0 = W["wte"][ids[b, :L0]].astype(np.float64) + W["wpe"][:L0]
+        h = oracle.round_bf16(oracle.layer_norm(x0, lw["ln1_w"], lw["ln1_b"]))
+        qkv = oracle.linear(h, lw["attn_w"], lw["attn_b"])
+        for which, bits in (("k", kb), ("v", vb)):
+            off = C if which == "k" else 2 * C
+            want = oracle.round_bf16(qkv[:, off:off + C]).reshape(L0, w.n_head, hs).transpose(1, 0, 2)
+            _, err = check_cache_stage(bits[b][:, :L0], want)
+            worst = max(worst, err)
+    ref = make_oracle(w, W).prefill(ids, lens)
+    ref_exact = make_exact_oracle(w, W).prefill(ids, lens)
+    e1, e2 = max_abs(got, ref), max_abs(got, ref_exact)
+    log(f"  2035-row prefill: layer-0 K/V largest abs diff {worst:.2e}; logits "
+        f"{e1:.2e} (bf16 mode) / {e2:.2e} (exact)")
+    assert e1 < TOL_BF16 and e2 < TOL_BF16
+    assert m.device_status() == 0
