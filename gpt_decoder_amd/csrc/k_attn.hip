@@ -38,8 +38,9 @@ constexpr int kPrefillKch = 8;   // key tiles per chunk when a prefill tile is s
 // lane holds one query column: lane l owns query q0 + 16*wave + (l % 16) and
 // keys 16*t + 4*(l/16) + i (i < 4) of each 16-key sub-tile t.  The running
 // softmax statistics are then per lane.  The output is formed as
-// O^T = V^T P^T; P^T is fed straight from the score registers, with V^T read
-// from a transposed LDS copy in the same key order.
+// O^T = V^T P^T; P^T is fed straight from the score registers, and the V^T
+// fragments are read from a key-major LDS copy of V by the transposing LDS
+// read (ds_read_b64_tr_b16) in the same key order.
 // ---------------------------------------------------------------------------
 //
 // With a past (chunked prefill into a live cache) the new rows of a
@@ -73,16 +74,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void attn_prefill_mfma(
   typedef typename Half16<T>::vec8 vec8;
   constexpr int KT = 64;             // keys per tile
   constexpr int KS = HS + 8;         // sK row stride (elements)
-  constexpr int VS = KT + 8;         // sVt row stride (elements)
+  // sV row stride (elements): 16 more than a row, so that the four keys one
+  // transposing read takes (32 bytes each) start 32 bytes apart modulo 128
+  constexpr int VS = HS + 16;
   constexpr int NKK = HS / 32;       // MFMA steps over the head dimension
   constexpr int ND = HS / 16;        // 16-row output sub-tiles over hs
   constexpr int MS = ND * 4 + 4;     // merge record per lane: o, then m, l
-  // V^T rows are stored with their key index XORed by 16 * ((dim / 8) % 4):
-  // the eight dims one staging store covers then fall in different LDS
-  // banks, and four consecutive keys stay adjacent for the fragment reads.
-  auto vswz = [](int dim) { return 16 * ((dim >> 3) & 3); };
   __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[HS * VS];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[KT * VS];
   __shared__ __attribute__((aligned(16))) float sM[4 * 64 * MS];
 
   int b, h, qt, chunk;
@@ -142,8 +141,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void attn_prefill_mfma(
 
   const int nkt = (nch > 1 ? min(kt0 + kch, nkt_all) : nkt_all) - kt0;
   // Staging work item: a pair of keys (2kp, 2kp+1) x 8 dims, of K for the
-  // first four wavefronts and of V for the other four; K goes to LDS
-  // key-major, V transposed (dim-major) with the two keys packed in 32 bits.
+  // first four wavefronts and of V for the other four; both go to LDS
+  // key-major.
   // S tiles are in flight in registers.  The loads are range-checked buffer
   // loads issued on every path, through a resource spanning the tile's 64
   // cache rows (one block): keys at or past len (whose cache rows may hold
@@ -177,17 +176,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void attn_prefill_mfma(
       *reinterpret_cast<uint4*>(sK + (2 * kp) * KS + d0) = rs[st][0];
       *reinterpret_cast<uint4*>(sK + (2 * kp + 1) * KS + d0) = rs[st][1];
     } else {
-      const uint32_t a[4] = {rs[st][0].x, rs[st][0].y, rs[st][0].z, rs[st][0].w};
-      const uint32_t b2[4] = {rs[st][1].x, rs[st][1].y, rs[st][1].z, rs[st][1].w};
-      const int kx = (2 * kp) ^ vswz(d0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // dims d0+2j (low halves) and d0+2j+1 (high halves) of the two keys
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j) * VS + kx) =
-            (a[j] & 0xFFFFu) | (b2[j] << 16);
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 2 * j + 1) * VS + kx) =
-            (a[j] >> 16) | (b2[j] & 0xFFFF0000u);
-      }
+      *reinterpret_cast<uint4*>(sV + (2 * kp) * VS + d0) = rs[st][0];
+      *reinterpret_cast<uint4*>(sV + (2 * kp + 1) * VS + d0) = rs[st][1];
     }
   };
 #pragma unroll
@@ -280,14 +270,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void attn_prefill_mfma(
       const uint32_t w3 = Half16<T>::pack2(s[1][2], s[1][3]);
       pf = __builtin_bit_cast(vec8, make_uint4(w0, w1, w2, w3));
     }
+    // V^T fragment of dims 16 d .. 16 d + 15: lane l needs dim 16 d + l % 16
+    // at keys e .. e + 3 and e + 16 .. e + 19 (e = 32 kh + 4 g), the key
+    // order of pf.  A transposing read hands lane j of a 16-lane group
+    // element j % 4 of rows j / 4 + 4 i (i = 0..3) of the 16 rows of four
+    // 16-bit values its lanes address; lane j addresses key e + j / 4,
+    // dims 16 d + 4 (j % 4) .. + 3, so it receives dim 16 d + j of keys
+    // e .. e + 3 in order.
+    {
+      const int jj = lane & 15, e = kh * 32 + g * 4;
+      const bf16_t* vb = sV + (e + (jj >> 2)) * VS + (jj & 3) * 4;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const int vrow = d * 16 + (lane & 15), e = kh * 32 + g * 4;
-      const bf16_t* vr = sVt + vrow * VS;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + (e ^ vswz(vrow)));
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((e + 16) ^ vswz(vrow)));
-      const vec8 vf = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      o[d] = Half16<T>::mfma(vf, pf, o[d]);
+      for (int d = 0; d < ND; ++d) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vb + d * 16));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(vb + 16 * VS + d * 16));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const vec8 vf = __builtin_bit_cast(vec8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        o[d] = Half16<T>::mfma(vf, pf, o[d]);
+      }
     }
   }
   }
