@@ -571,7 +571,15 @@ __global__ __launch_bounds__(64) void gemv_kernel(
   const int lane = threadIdx.x;
   const int n0 = blockIdx.x * CPW;
 
-  // 1. every load of this lane, issued before any of them is used
+  // 1. every load of this lane, issued before any of them is used, through
+  // range-checked buffer loads: a lane past K (the last chunk of a K that is
+  // not a multiple of the span) or a row past M reads zeros, and no load
+  // sits behind a per-lane branch (each such load was waited for before the
+  // next was issued)
+  constexpr uint32_t kOut = 0x80000000u;   // offset past every buffer: reads 0
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * (uint32_t)sizeof(T)),
+      0x00020000);
   uint4 wv[NCH][CPW];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
@@ -579,14 +587,20 @@ __global__ __launch_bounds__(64) void gemv_kernel(
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int n = min(n0 + c, N - 1);
-      wv[j][c] = (k < K) ? *reinterpret_cast<const uint4*>(W + (size_t)n * K + k)
-                         : make_uint4(0, 0, 0, 0);
+      wv[j][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          rw, k < K ? ((uint32_t)n * (uint32_t)K + (uint32_t)k) * (uint32_t)sizeof(T) : kOut,
+          0, 0));
     }
   }
   // A rows: LN keeps the raw fp32 x values (normalised below); otherwise the
   // packed 16-byte vectors are kept and widened at use
   float av[LN ? MR : 1][LN ? NCH : 1][VE];
   uint4 araw[LN ? 1 : MR][LN ? 1 : NCH];
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      LN ? const_cast<float*>(ln.x) : static_cast<void*>(const_cast<T*>(A)), (short)0,
+      LN ? (int)((uint32_t)M * (uint32_t)ln.ldx * 4u)
+         : (int)((uint32_t)M * (uint32_t)lda * (uint32_t)sizeof(T)),
+      0x00020000);
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
@@ -594,17 +608,18 @@ __global__ __launch_bounds__(64) void gemv_kernel(
       const int k = j * SPAN + lane * VE;
       const bool ok = m < M && k < K;
       if constexpr (LN) {
-        const float* xr = ln.x + (size_t)m * ln.ldx + k;
+        const uint32_t xo = ok ? ((uint32_t)m * (uint32_t)ln.ldx + (uint32_t)k) * 4u : kOut;
 #pragma unroll
         for (int q = 0; q < VE; q += 4) {
-          const float4 t4 = ok ? *reinterpret_cast<const float4*>(xr + q)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 t4 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+              ra, xo == kOut ? kOut : xo + (uint32_t)q * 4u, 0, 0));
           av[m][j][q] = t4.x; av[m][j][q + 1] = t4.y;
           av[m][j][q + 2] = t4.z; av[m][j][q + 3] = t4.w;
         }
       } else {
-        araw[m][j] = ok ? *reinterpret_cast<const uint4*>(A + (size_t)m * lda + k)
-                        : make_uint4(0, 0, 0, 0);
+        araw[m][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            ra, ok ? ((uint32_t)m * (uint32_t)lda + (uint32_t)k) * (uint32_t)sizeof(T) : kOut,
+            0, 0));
       }
     }
 
