@@ -743,6 +743,11 @@ __global__ __launch_bounds__(256) void attn_proj_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * kProjCols + wave * CPW;
 
+  // weight loads first, range-checked on every path (lanes past K read 0)
+  constexpr uint32_t kOut = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(W), (short)0, (int)((uint32_t)N * (uint32_t)K * (uint32_t)sizeof(T)),
+      0x00020000);
   uint4 wv[NCH][CPW];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
@@ -750,8 +755,9 @@ __global__ __launch_bounds__(256) void attn_proj_kernel(
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int n = min(n0 + c, N - 1);
-      wv[j][c] = (k < K) ? *reinterpret_cast<const uint4*>(W + (size_t)n * K + k)
-                         : make_uint4(0, 0, 0, 0);
+      wv[j][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          rw, k < K ? ((uint32_t)n * (uint32_t)K + (uint32_t)k) * (uint32_t)sizeof(T) : kOut,
+          0, 0));
     }
   }
 
